@@ -1,0 +1,397 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each check ties the oracle to something other than itself: torch's CPU casts
+(exhaustive over every code), float64 scaled-dot-product attention (the
+multi-query special case of MLA decode), a pure-Python brute force, closed
+forms, split/merge identities, and deliberately wrong variants that must be
+rejected by the same gate the GPU parity tests use.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import formats, mla
+from mla_decode_paged_split_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL, ATOL, NORM_GATE = 2e-2, 1e-2, 1e-2
+
+
+def gate(ref, got):
+    """The parity gate: elementwise allclose AND normwise relative error."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    ok_elem = bool(np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref)))
+    nrm = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    return ok_elem and nrm <= NORM_GATE
+
+
+# ----------------------------------------------------------------- page constants
+
+
+def test_constants_match_pages():
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        g = json.load(f)
+    assert mla.NUM_HEADS == g["num_heads"]
+    assert mla.QK_DIM == g["qk_head_dim"]
+    assert mla.V_DIM == g["v_head_dim"]
+    assert mla.SM_SCALE == 1.0 / math.sqrt(g["qk_head_dim"]) == 1.0 / 24.0
+    finite = formats.FP8_TABLE[np.isfinite(formats.FP8_TABLE)]
+    assert finite.max() == g["fp8_e4m3_range"][1] and finite.min() == g["fp8_e4m3_range"][0]
+
+
+# ----------------------------------------------------------------- number formats
+
+
+def test_bf16_decode_exhaustive_vs_torch():
+    codes = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float64).numpy()
+    got = formats.decode_bf16(codes.numpy())
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    # signed zeros and infinities keep their sign
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_fp8_decode_exhaustive_vs_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = formats.decode_fp8_e4m3fn(codes.numpy())
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+    assert got[1] == 2.0 ** -9 and np.nanmax(got) == 448.0
+
+
+def test_fp8_cast_exhaustive_over_bf16_vs_torch():
+    codes = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = formats.bf16_bits_to_fp8_bits(codes.numpy())
+    assert np.array_equal(ref, got)
+
+
+def test_fp8_cast_float_edges_vs_torch():
+    rng = np.random.default_rng(7)
+    vals = np.concatenate(
+        [
+            rng.standard_normal(4000) * 3,
+            rng.standard_normal(2000) * 200,
+            rng.standard_normal(2000) * 1e-3,
+            np.array([0.0, -0.0, 448, 456, 464, 464.0001, 465, -464, -465, 2**-9, 2**-10, 3 * 2**-11,
+                      2**-6, 2**-6 - 2**-12, 1.0625, 1.1875, 1e30, -1e30]),
+        ]
+    ).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = formats.encode_fp8_e4m3fn(vals.astype(np.float64))
+    assert np.array_equal(ref, got)
+
+
+def test_bf16_rne_vs_torch():
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([rng.standard_normal(3000), rng.standard_normal(500) * 1e-39,
+                           np.array([1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 0.0, -0.0])])
+    # float64 -> bf16 directly; compare with torch where float32 holds the value exactly
+    v32 = vals.astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = formats.encode_bf16_rne(v32)
+    assert np.array_equal(ref, got)
+
+
+# ------------------------------------------------------------ attention special cases
+
+
+def _rand_case(rng, B, lens, dtype_q="bf16", dtype_kv="bf16", permute=False):
+    total = int(sum(lens))
+    q32 = torch.from_numpy(rng.standard_normal((B, 16, 576)).astype(np.float32))
+    kv32 = torch.from_numpy(rng.standard_normal((total, 576)).astype(np.float32))
+    q_bits = q32.to(torch.bfloat16).view(torch.int16).numpy()
+    if dtype_kv == "bf16":
+        kv_bits = kv32.to(torch.bfloat16).view(torch.int16).numpy()
+        kv_scale = None
+    else:
+        kv_scale = float((kv32.abs().max() / 448.0).item())
+        kv_bits = (kv32 / kv_scale).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    kv_indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = rng.permutation(total) if permute else np.arange(total)
+    # when permuting, physically move rows so that the logical sequence is unchanged
+    if permute:
+        moved = np.empty_like(kv_bits)
+        moved[idx] = kv_bits
+        kv_bits = moved
+    return q_bits, kv_bits, np.arange(B + 1), kv_indptr, idx, kv_scale
+
+
+def _sdpa_reference(q_bits, kv_bits, kv_indptr, kv_indices, kv_dtype, kv_scale, q_dtype="bf16", q_scale=None):
+    """torch float64 scaled_dot_product_attention, K/V broadcast to 16 heads."""
+    B = len(kv_indptr) - 1
+    out = []
+    for b in range(B):
+        rows = np.asarray(kv_indices[kv_indptr[b]: kv_indptr[b + 1]])
+        if q_dtype == "bf16":
+            Q = torch.from_numpy(q_bits[b]).view(torch.bfloat16).to(torch.float64)
+        else:
+            Q = torch.from_numpy(q_bits[b]).view(torch.float8_e4m3fn).to(torch.float64) * q_scale
+        if kv_dtype == "bf16":
+            K = torch.from_numpy(kv_bits[rows]).view(torch.bfloat16).to(torch.float64)
+        else:
+            K = torch.from_numpy(kv_bits[rows]).view(torch.float8_e4m3fn).to(torch.float64) * kv_scale
+        q4 = Q[None, :, None, :]  # [1, H, 1, 576]
+        k4 = K[None, None].expand(1, 16, K.shape[0], 576)
+        v4 = K[:, :512][None, None].expand(1, 16, K.shape[0], 512)
+        o = torch.nn.functional.scaled_dot_product_attention(q4, k4, v4, scale=1.0 / 24.0)
+        out.append(o[0, :, 0, :].numpy())
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_oracle_vs_sdpa_float64(kv_dtype):
+    rng = np.random.default_rng(11)
+    lens = [1, 2, 17, 64, 300, 1000]
+    q_bits, kv_bits, qo, kvp, idx, kvs = _rand_case(rng, len(lens), lens, dtype_kv=kv_dtype, permute=True)
+    got = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype=kv_dtype, kv_scale=kvs)
+    ref = _sdpa_reference(q_bits, kv_bits, kvp, idx, kv_dtype, kvs)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_oracle_vs_sdpa_fp8_q():
+    rng = np.random.default_rng(12)
+    lens = [5, 129, 700]
+    q_bits, kv_bits, qo, kvp, idx, kvs = _rand_case(rng, 3, lens, dtype_kv="fp8")
+    q8 = formats.bf16_bits_to_fp8_bits(q_bits)
+    q_scale = 1.0
+    got = oracle.mla_decode(q8, kv_bits, qo, kvp, idx, q_dtype="fp8", kv_dtype="fp8", q_scale=q_scale, kv_scale=kvs)
+    ref = _sdpa_reference(q8, kv_bits, kvp, idx, "fp8", kvs, q_dtype="fp8", q_scale=q_scale)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_oracle_vs_bruteforce_tiny():
+    rng = np.random.default_rng(5)
+    lens = [1, 3, 5]
+    q_bits, kv_bits, qo, kvp, idx, _ = _rand_case(rng, 3, lens, permute=True)
+    got = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16")
+    for b in range(3):
+        Q = formats.decode_bf16(q_bits[b]).tolist()
+        K = [formats.decode_bf16(kv_bits[idx[i]]).tolist() for i in range(kvp[b], kvp[b + 1])]
+        bf = np.array(mla.mla_decode_bruteforce(Q, K, 1.0 / 24.0, 512))
+        assert np.max(np.abs(bf - got[b])) <= 1e-12
+
+
+# ------------------------------------------------------------------- closed forms
+
+
+def _seq(rng, n, scale=1.0):
+    Q = rng.standard_normal((16, 576)) * scale
+    K = rng.standard_normal((n, 576))
+    return Q, K
+
+
+def test_single_row_returns_its_v():
+    rng = np.random.default_rng(1)
+    Q, K = _seq(rng, 1, 10.0)
+    O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+    assert np.array_equal(O, np.broadcast_to(K[0, :512], O.shape))
+
+
+def test_zero_query_returns_mean_of_v():
+    rng = np.random.default_rng(2)
+    _, K = _seq(rng, 37)
+    O = mla.mla_decode_sequence(np.zeros((16, 576)), K, mla.SM_SCALE)
+    assert np.max(np.abs(O - K[:, :512].mean(axis=0))) <= 1e-13
+
+
+def test_constant_v_returns_constant():
+    rng = np.random.default_rng(3)
+    Q, K = _seq(rng, 50, 3.0)
+    c = rng.standard_normal(512)
+    K[:, :512] = c  # rope dims stay random, so scores still differ
+    O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+    assert np.max(np.abs(O - c)) <= 1e-13
+
+
+def test_two_rows_logistic():
+    rng = np.random.default_rng(4)
+    Q, K = _seq(rng, 2)
+    s = mla.SM_SCALE * (Q @ K.T)
+    w1 = 1.0 / (1.0 + np.exp(s[:, 1] - s[:, 0]))
+    expect = w1[:, None] * K[0, :512] + (1 - w1)[:, None] * K[1, :512]
+    O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+    assert np.max(np.abs(O - expect)) <= 1e-13
+
+
+def test_dominant_row_no_overflow():
+    rng = np.random.default_rng(5)
+    Q, K = _seq(rng, 64)
+    # row 7 aligned with head 0's query and scaled so its score leads by > 40
+    K[7] = Q[0] / np.linalg.norm(Q[0]) * 24.0 * 60.0 / np.linalg.norm(Q[0])
+    O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+    assert np.all(np.isfinite(O))
+    assert np.max(np.abs(O[0] - K[7, :512])) <= 1e-12 * np.max(np.abs(K[7, :512])) + 1e-12
+
+
+def test_duplicate_row_equals_ln2_bias():
+    rng = np.random.default_rng(6)
+    Q, K = _seq(rng, 20)
+    dup = np.concatenate([K, K[3:4]], axis=0)
+    O_dup = mla.mla_decode_sequence(Q, dup, mla.SM_SCALE)
+    s = mla.SM_SCALE * (Q @ K.T)
+    s[:, 3] += math.log(2.0)
+    P = np.exp(s - s.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(O_dup - P @ K[:, :512])) <= 1e-13
+
+
+def test_empty_sequence_is_zero():
+    O = mla.mla_decode_sequence(np.ones((16, 576)), np.zeros((0, 576)), mla.SM_SCALE)
+    assert np.array_equal(O, np.zeros((16, 512)))
+
+
+# ------------------------------------------------------------- split / merge
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 3, 7, 40])
+def test_split_merge_equals_unsplit(nsplit):
+    rng = np.random.default_rng(100 + nsplit)
+    Q, K = _seq(rng, 333, 2.0)
+    cuts = np.sort(rng.choice(np.arange(1, 333), size=nsplit - 1, replace=False)) if nsplit > 1 else []
+    bounds = [0, *cuts, 333]
+    parts = [mla.attention_partial(Q, K[a:b], mla.SM_SCALE) for a, b in zip(bounds[:-1], bounds[1:])]
+    O = mla.merge_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    assert np.max(np.abs(O - mla.mla_decode_sequence(Q, K, mla.SM_SCALE))) <= 1e-13
+
+
+def test_merge_ignores_empty_parts_and_all_empty_is_zero():
+    rng = np.random.default_rng(9)
+    Q, K = _seq(rng, 10)
+    p_full = mla.attention_partial(Q, K, mla.SM_SCALE)
+    p_empty = mla.attention_partial(Q, K[:0], mla.SM_SCALE)
+    assert np.all(np.isneginf(p_empty[1]))
+    O = mla.merge_partials(np.stack([p_empty[0], p_full[0]]), np.stack([p_empty[1], p_full[1]]))
+    assert np.max(np.abs(O - mla.mla_decode_sequence(Q, K, mla.SM_SCALE))) <= 1e-14
+    Z = mla.merge_partials(np.stack([p_empty[0]] * 3), np.stack([p_empty[1]] * 3))
+    assert np.array_equal(Z, np.zeros_like(Z))
+
+
+def test_lse_is_log_sum_exp():
+    rng = np.random.default_rng(10)
+    Q, K = _seq(rng, 30)
+    _, lse = mla.attention_partial(Q, K, mla.SM_SCALE)
+    s = mla.SM_SCALE * (Q @ K.T)
+    assert np.max(np.abs(lse - np.log(np.exp(s).sum(axis=1)))) <= 1e-12
+
+
+# -------------------------------------------------------------------- invariants
+
+
+def test_pool_permutation_invariance():
+    rng = np.random.default_rng(21)
+    lens = [40, 1, 90]
+    q_bits, kv_bits, qo, kvp, idx, _ = _rand_case(rng, 3, lens, permute=False)
+    a = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16")
+    perm = rng.permutation(kv_bits.shape[0])
+    moved = np.empty_like(kv_bits)
+    moved[perm] = kv_bits
+    b = oracle.mla_decode(q_bits, moved, qo, kvp, perm[idx], q_dtype="bf16", kv_dtype="bf16")
+    assert np.array_equal(a, b)
+
+
+def test_head_permutation_and_scale_trade():
+    rng = np.random.default_rng(22)
+    Q, K = _seq(rng, 70)
+    perm = rng.permutation(16)
+    O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+    assert np.max(np.abs(mla.mla_decode_sequence(Q[perm], K, mla.SM_SCALE) - O[perm])) <= 1e-14
+    assert np.max(np.abs(mla.mla_decode_sequence(Q / 4.0, K, mla.SM_SCALE * 4.0) - O)) <= 1e-13
+
+
+def test_sequences_are_independent():
+    rng = np.random.default_rng(23)
+    lens = [50, 60]
+    q_bits, kv_bits, qo, kvp, idx, _ = _rand_case(rng, 2, lens)
+    a = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16")
+    kv2 = kv_bits.copy()
+    kv2[60:] = kv2[60:][::-1]  # scramble sequence 1's rows only
+    b = oracle.mla_decode(q_bits, kv2, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16")
+    assert np.array_equal(a[0], b[0]) and not np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------- mutation checks
+
+
+def _mutants():
+    """Plausible mistakes in an MLA-decode implementation, planted on the CPU."""
+
+    def no_rope(Q, K):
+        return mla.mla_decode_sequence(Q[:, :512], K[:, :512], mla.SM_SCALE)
+
+    def wrong_scale(Q, K):
+        return mla.mla_decode_sequence(Q, K, 1.0 / math.sqrt(512.0))
+
+    def v_from_tail(Q, K):
+        S = mla.SM_SCALE * Q @ K.T
+        P = np.exp(S - S.max(1, keepdims=True))
+        P /= P.sum(1, keepdims=True)
+        return P @ K[:, 64:]
+
+    def drop_last_row(Q, K):
+        return mla.mla_decode_sequence(Q, K[:-1], mla.SM_SCALE)
+
+    def no_max_subtract_but_wrong_sign(Q, K):
+        return mla.mla_decode_sequence(-Q, K, mla.SM_SCALE)
+
+    def head_swap(Q, K):
+        return mla.mla_decode_sequence(Q[::-1].copy(), K, mla.SM_SCALE)[::-1]
+
+    def first_head_only(Q, K):
+        O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+        return np.broadcast_to(O[0], O.shape)
+
+    return [no_rope, wrong_scale, v_from_tail, drop_last_row, no_max_subtract_but_wrong_sign, first_head_only]
+
+
+@pytest.mark.parametrize("n", [1024, 8192])
+def test_mutants_fail_the_gate(n):
+    rng = np.random.default_rng(31 + n)
+    Q = formats.decode_bf16(torch.from_numpy(rng.standard_normal((16, 576)).astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy())
+    K = formats.decode_bf16(torch.from_numpy(rng.standard_normal((n, 576)).astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy())
+    ref = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+    # the true result rounded to bf16 passes
+    rounded = formats.decode_bf16(formats.encode_bf16_rne(ref[:2]))
+    assert gate(ref[:2], rounded)
+    for mut in _mutants():
+        if mut.__name__ == "drop_last_row" and n > 1024:
+            continue  # one row in 8192 is below any bf16-level gate; checked at n=1024 only
+        got = mut(Q, K)
+        assert not gate(ref, got), mut.__name__
+
+
+def test_mutant_missing_kv_scale_fails():
+    rng = np.random.default_rng(41)
+    lens = [256, 512]
+    q_bits, kv_bits, qo, kvp, idx, kvs = _rand_case(rng, 2, lens, dtype_kv="fp8")
+    ref = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="fp8", kv_scale=kvs)
+    bad = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="fp8", kv_scale=1.0)
+    assert not gate(ref, bad)
+
+
+# -------------------------------------------------------------------- generator
+
+
+def test_generator_is_seeded_and_shaped():
+    spec = synth.CaseSpec(batch=5, q_dtype="bf16", kv_dtype="fp8", ragged_max=300, permuted=True, seed=77)
+    a = synth.make_case(spec)
+    b = synth.make_case(spec)
+    assert torch.equal(a.kv.view(torch.uint8), b.kv.view(torch.uint8)) and torch.equal(a.kv_indices, b.kv_indices)
+    assert a.q_bf16.shape == (5, 16, 576) and a.kv.shape == (int(a.lengths.sum()), 576)
+    assert int(a.kv_indptr[-1]) == int(a.lengths.sum()) and a.lengths.min() >= 1
+    assert sorted(a.kv_indices.tolist()) == list(range(a.kv.shape[0]))
+    # per-tensor scale maps the largest magnitude onto the fp8 maximum
+    assert a.kv.view(torch.uint8).numpy().view(np.uint8).max() in (0x7E, 0xFE) or \
+        np.abs(formats.decode_fp8_e4m3fn(a.kv.view(torch.uint8).numpy())).max() == 448.0
