@@ -1,0 +1,274 @@
+"""Benchmark one MLA-decode step on one MI355X and print one JSON line.
+
+A step is one pass of the whole path over one batch: the fp8 cast of Q when
+the workload has fp8 queries (step a0), then one mla_decode_run (work split,
+split attention and the merge of split partials).  The plan is made once: it
+does not depend on the sequence lengths.
+
+Inputs are seeded synthetic tensors of the workload's shapes, resident in HBM
+before the timed region.  The KV pool and its indices are replicated R times
+(R copies together >= 1 GiB) and the steps rotate through the copies, so a
+step cannot be served from the 256 MB last-level cache left warm by the
+previous step.
+
+Throughput is reported as algorithmic HBM bytes per second: KV rows read
+(576 B for fp8, 1152 B for bf16) + 4 B kv_indices per row + Q + bf16 output +
+both indptrs.  The split partials are implementation overhead and are not
+counted; their traffic shows up in the FETCH_SIZE / WRITE_SIZE counters.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "m_bf16q_fp8kv_b64_kv8192"
+KERNEL_SOURCES = ["mla_decode_paged_split_amd/csrc/mla_device.hpp", "mla_decode_paged_split_amd/csrc/mla_decode.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(spec, total_kv: int, q_elt: int) -> int:
+    kv_elt = 1 if spec.kv_dtype == "fp8" else 2
+    B = spec.batch
+    return total_kv * 576 * kv_elt + total_kv * 4 + B * 16 * 576 * q_elt + B * 16 * 512 * 2 + 2 * (B + 1) * 4
+
+
+def workload_label(spec) -> str:
+    lens = f"kv{spec.kv_len}" if not spec.ragged_max else f"kv U[1,{spec.ragged_max}] permuted"
+    return f"MLA decode b{spec.batch} {lens} {spec.q_dtype}-Q {spec.kv_dtype}-KV page_size=1"
+
+
+def load_traffic(workload: str, launches_per_step: int):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"mla_decode_kernel_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the float64 oracle on whole sequences until about budget_s of CPU work."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q_bits = case.q_bits().numpy()
+    if case.spec.q_dtype == "fp8":
+        q_bits = oracle.bf16_bits_to_fp8_bits(q_bits)
+    kv_bits = case.kv_bits().numpy()
+    qo = case.qo_indptr.numpy()
+    kvp = case.kv_indptr.numpy()
+    idx = case.kv_indices.numpy()
+    kv_scale = float(case.kv_scale[0]) if case.kv_scale is not None else None
+    q_scale = 1.0 if case.spec.q_dtype == "fp8" else None
+    done = []
+    t0 = time.perf_counter()
+    for b in range(case.spec.batch):
+        oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype=case.spec.q_dtype, kv_dtype=case.spec.kv_dtype,
+                          q_scale=q_scale, kv_scale=kv_scale, sequences=[b])
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    rows = int(sum(int(kvp[b + 1] - kvp[b]) for b in done))
+    kv_elt = 1 if case.spec.kv_dtype == "fp8" else 2
+    q_elt = 1 if case.spec.q_dtype == "fp8" else 2
+    nb = len(done)
+    bytes_done = rows * (576 * kv_elt + 4) + nb * (16 * 576 * q_elt + 16 * 512 * 2 + 8)
+    return {
+        "value": bytes_done / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{nb} of {case.spec.batch} sequences ({rows} KV rows), float64 numpy, {dt:.1f} s",
+        "us_per_call_extrapolated": dt / nb * case.spec.batch * 1e6,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--rotate-bytes", type=float, default=2**30, help="KV bytes to rotate through (cache defeat)")
+    ap.add_argument("--num-units", type=int, default=0)
+    ap.add_argument("--min-chunk", type=int, default=0)
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--probe-copy", action="store_true", help="time a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path runs on a single device.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from mla_decode_paged_split_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+
+    if args.probe_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 10
+        print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": dt * 1e3,
+                          "GBps_read_plus_write": 2 * n / dt / 1e9}))
+        return 0
+
+    spec = synth.CONFIGS[args.workload]
+    case = synth.make_case(spec)
+    total_kv = case.total_kv
+    kv_bytes_one = case.kv.numel() * case.kv.element_size()
+    R = max(1, min(16, math.ceil(args.rotate_bytes / max(kv_bytes_one, 1))))
+
+    q_bf16 = case.q_bf16.to(dev)
+    kvs = [case.kv.to(dev) for _ in range(R)]
+    idxs = [case.kv_indices.to(dev) for _ in range(R)]
+    qo_indptr = case.qo_indptr.to(dev)
+    kv_indptr = case.kv_indptr.to(dev)
+    kv_scale = case.kv_scale.to(dev) if case.kv_scale is not None else None
+    fp8_q = spec.q_dtype == "fp8"
+    q_in = torch.empty(q_bf16.shape, dtype=torch.uint8, device=dev) if fp8_q else q_bf16
+    q_scale = torch.ones(1, dtype=torch.float32, device=dev) if fp8_q else None
+    out = torch.empty((spec.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+    dec = binding.Decoder(spec.batch, spec.q_dtype, spec.kv_dtype, dev, num_units=args.num_units,
+                          min_chunk=args.min_chunk, flags=args.flags)
+    sm_scale = 1.0 / 24.0
+    stream = torch.cuda.current_stream()
+
+    def step(i: int, ev=None):
+        r = i % R
+        if fp8_q:
+            binding.mla_decode_quantize_q(q_bf16, q_in, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        dec.run(q_in, kvs[r], qo_indptr, kv_indptr, idxs[r], q_scale, kv_scale, sm_scale, out, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: whole steps back to back
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # timed region 2: the attention launch alone, bracketed by events on its stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    kern_med_ms = kern_ms[len(kern_ms) // 2]
+
+    q_elt = 1 if fp8_q else 2
+    alg_bytes = algorithmic_bytes(spec, total_kv, q_elt)
+    step_bytes = alg_bytes + (q_bf16.numel() * 3 if fp8_q else 0)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, 1)
+
+    res = {
+        "metric": "MLA decode µs/call + achieved HBM GB/s (% peak), bs=64 kv=8192 fp8 KV",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not fp8_q else "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": workload_label(spec),
+            "batch": spec.batch,
+            "q_seq_len": 1,
+            "kv_len": spec.kv_len if not spec.ragged_max else f"U[1,{spec.ragged_max}]",
+            "total_kv_rows": total_kv,
+            "q_dtype": spec.q_dtype,
+            "kv_dtype": spec.kv_dtype,
+            "heads": 16,
+            "qk_dim": 576,
+            "v_dim": 512,
+            "page_size": 1,
+            "kv_copies_rotated": R,
+            "num_units": int(dec.plan.params.num_units),
+            "min_chunk": int(dec.plan.params.min_chunk),
+            "fused_merge": not (args.flags & 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "mla_decode_kernel",
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
+            "kernel_median_us": round(kern_med_ms * 1e3, 2),
+        },
+        "wall_s_timed": round(wall, 4),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

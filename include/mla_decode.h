@@ -1,0 +1,172 @@
+/*
+ * libmla_decode -- paged multi-head latent attention (MLA) decode for MI355X (gfx950).
+ *
+ * What one call computes (kernelindex amd-mixed-mla submission 689529, module
+ * constants block and custom_kernel; submission 690201, the stage-1 and
+ * reduce calls):
+ *
+ *   for every sequence b and its query token t = qo_indptr[b]:
+ *     rows  j_i = kv_indices[i], i in [kv_indptr[b], kv_indptr[b+1])
+ *     s_i   = sm_scale * q_scale * kv_scale * sum_{d<576} q[t,h,d] * kv[j_i,d]
+ *     out[t,h,e] = kv_scale * sum_i softmax(s)_i * kv[j_i,e]     (e < 512)
+ *
+ * for all 16 heads h.  The single latent KV head is 576 wide (512 latent +
+ * 64 rope); V is the first 512 dims of the same row.  Pages hold one row
+ * (page size 1), so a row index is a page index.
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   q          [total_q, 16, 576]   bf16 or fp8 e4m3fn
+ *   kv         [pool_rows, 576]     bf16 or fp8 e4m3fn (one KV head, page size 1)
+ *   qo_indptr  [batch + 1]          int32, query rows of sequence b
+ *   kv_indptr  [batch + 1]          int32, index positions of sequence b
+ *   kv_indices [kv_indptr[batch]]   int32, pool row of each index position
+ *   out        [total_q, 16, 512]   bf16
+ *   q_scale, kv_scale               one float32 each, in device memory
+ *                                   (read only for fp8 operands; may be NULL
+ *                                   for bf16 operands)
+ *
+ * Supported dtype pairs (q, kv): (bf16, bf16), (bf16, fp8), (fp8, fp8).
+ * fp8 is the OCP e4m3fn format (max 448, no infinities).
+ *
+ * Ownership and threading: the caller owns every buffer, the workspace
+ * included.  The library never allocates device memory and never
+ * synchronises a stream; all work is enqueued on the stream passed in.
+ * One workspace must not be used by two calls that may overlap in time
+ * (e.g. on two streams): the calls share its partial buffers and counters.
+ *
+ * Errors: every entry point returns mla_status.  Arguments are validated on
+ * the host before any HIP call; a rejected call enqueues nothing.  A HIP
+ * launch failure is reported as MLA_ERR_HIP.  Index values (kv_indices,
+ * qo_indptr) are not checked on the device: out-of-range values are a caller
+ * error and lead to undefined results.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_DECODE_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent params */
+  MLA_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels implement */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP8_E4M3FN = 1 } mla_dtype;
+
+/* Flags for mla_decode_params.flags. */
+#define MLA_FLAG_SEPARATE_REDUCE 1u /* merge split partials in a second kernel
+                                       instead of in the last workgroup of each
+                                       split sequence */
+
+/*
+ * Problem description.  The fixed fields restate the model constants of
+ * submission 689529 (16 heads, 1 KV head, 576 / 512 dims, page size 1);
+ * anything else is MLA_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  int32_t batch;        /* sequences, >= 1 */
+  int32_t total_q;      /* query rows; must equal batch (one decode token per sequence) */
+  int32_t num_heads;    /* 16 */
+  int32_t num_kv_heads; /* 1 */
+  int32_t qk_dim;       /* 576 */
+  int32_t v_dim;        /* 512 */
+  int32_t page_size;    /* 1 */
+  int32_t q_dtype;      /* mla_dtype */
+  int32_t kv_dtype;     /* mla_dtype */
+  int32_t num_units;    /* 0 = the device's compute-unit count.  Upper bound on the
+                           workgroups that split the KV rows; each one owns a
+                           contiguous share of all sequences' rows. */
+  int32_t min_chunk;    /* 0 = default (256).  Smallest share of KV rows per workgroup;
+                           must be a multiple of 32 when set. */
+  uint32_t flags;       /* MLA_FLAG_* */
+} mla_decode_params;
+
+/*
+ * A plan: validated parameters plus the workspace carve-up.  Plain data; it
+ * may be copied.  It stays valid as long as its workspace is alive.  It does
+ * not depend on the contents of kv_indptr: the split of KV rows over
+ * workgroups is recomputed on the device by every mla_decode_run from the
+ * kv_indptr passed to it, so sequence lengths may change between calls.
+ */
+typedef struct {
+  mla_decode_params params; /* with num_units / min_chunk resolved */
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t device;
+  int32_t reserved;
+  uint64_t off_counters; /* int32 [batch]: arrivals per split sequence, left at 0 after each run */
+  uint64_t off_part_o;   /* float32 [2 * num_units, 16, 512]: normalised split partials */
+  uint64_t off_part_lse; /* float32 [2 * num_units, 16]: log2-sum-exp of each partial */
+} mla_decode_plan_t;
+
+/* Bytes of device workspace mla_decode_plan needs for these params; 0 if the
+ * params are invalid or the device cannot be queried. */
+size_t mla_decode_workspace_size(const mla_decode_params* params);
+
+/*
+ * Validate params, resolve defaults against the current HIP device, carve
+ * the workspace and zero its counters (one small kernel on `stream`).
+ * workspace: device memory of at least mla_decode_workspace_size(params)
+ * bytes, 256-byte aligned, owned by the caller.  On success *plan is filled.
+ */
+mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, mla_decode_plan_t* plan);
+
+/*
+ * Enqueue one decode step on `stream` (kernelindex amd-mixed-mla submission
+ * 690201: stage-1 split attention then the partial reduce; here the split is
+ * chosen on the device and the reduce is folded into the same launch unless
+ * MLA_FLAG_SEPARATE_REDUCE is set).  Pointers as in the layout table above;
+ * sm_scale is a host float (1/sqrt(576) in the pages).  Sequences with no KV
+ * rows produce zeros.
+ */
+mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv,
+                          const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                          const float* q_scale, const float* kv_scale, float sm_scale, void* out,
+                          hipStream_t stream);
+
+/*
+ * Step a0 for fp8 queries: cast n bf16 values to fp8 e4m3fn with
+ * round-to-nearest-even and no saturation (|x| > 464, +-inf and NaN become
+ * the NaN code with the input's sign), as the pages cast Q straight to fp8
+ * with a unit scale (submission 689529 docstring and custom_kernel).
+ * q_bf16 and q_fp8 are device buffers of n elements; they must not overlap.
+ */
+mla_status mla_decode_quantize_q(const void* q_bf16, void* q_fp8, int64_t n, hipStream_t stream);
+
+/*
+ * Merge split partials produced elsewhere (e.g. KV shards on other devices):
+ * for every sequence b and head h, with p in [part_indptr[b], part_indptr[b+1]),
+ *   w_p = exp(lse[p,h] - max_p lse[p,h]),  out[b,h,:] = sum_p w_p o[p,h,:] / sum_p w_p
+ * rounded to bf16 (submission 690201: mla_reduce_v1 over logits / attn_lse).
+ *   part_o   [n_parts, 16, 512] float32, softmax-normalised over each part
+ *   part_lse [n_parts, 16] float32, natural-log sum-exp of each part's scores
+ *   out      [batch, 16, 512] bf16
+ * Parts with lse = -inf carry no weight; a sequence whose parts are all empty
+ * (or that has none) gets zeros.
+ */
+mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const int32_t* part_indptr,
+                             int32_t batch, void* out, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status status);
+
+/* MLA_DECODE_ABI_VERSION of the built library. */
+int32_t mla_decode_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,226 @@
+"""Thin ctypes binding over libmla_decode.so (argument marshalling only).
+
+Every entry point keeps the C name from ``include/mla_decode.h``.  torch is
+used only to own device memory and to name the current stream; all of the
+computation happens in the library's HIP kernels.  There is no fallback: if
+the library is missing or a call fails, a RuntimeError is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MLA_OK",
+    "MLA_ERR_INVALID_ARG",
+    "MLA_ERR_UNSUPPORTED",
+    "MLA_ERR_WORKSPACE",
+    "MLA_ERR_HIP",
+    "MLA_DTYPE_BF16",
+    "MLA_DTYPE_FP8_E4M3FN",
+    "MLA_FLAG_SEPARATE_REDUCE",
+    "MlaDecodeParams",
+    "MlaDecodePlan",
+    "library_path",
+    "lib",
+    "mla_status_string",
+    "mla_decode_abi_version",
+    "mla_decode_workspace_size",
+    "mla_decode_plan",
+    "mla_decode_run",
+    "mla_decode_quantize_q",
+    "mla_decode_reduce",
+    "make_params",
+    "Decoder",
+]
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE = 3
+MLA_ERR_HIP = 4
+MLA_DTYPE_BF16 = 0
+MLA_DTYPE_FP8_E4M3FN = 1
+MLA_FLAG_SEPARATE_REDUCE = 1
+
+_DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3FN}
+
+
+class MlaDecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("qk_dim", ctypes.c_int32),
+        ("v_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("num_units", ctypes.c_int32),
+        ("min_chunk", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class MlaDecodePlan(ctypes.Structure):
+    _fields_ = [
+        ("params", MlaDecodeParams),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("device", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("off_counters", ctypes.c_uint64),
+        ("off_part_o", ctypes.c_uint64),
+        ("off_part_lse", ctypes.c_uint64),
+    ]
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(path)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_decode_abi_version.argtypes = []
+        L.mla_decode_abi_version.restype = i32
+        L.mla_decode_workspace_size.argtypes = [ctypes.POINTER(MlaDecodeParams)]
+        L.mla_decode_workspace_size.restype = sz
+        L.mla_decode_plan.argtypes = [ctypes.POINTER(MlaDecodeParams), vp, sz, vp, ctypes.POINTER(MlaDecodePlan)]
+        L.mla_decode_plan.restype = ctypes.c_int
+        L.mla_decode_run.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
+        L.mla_decode_run.restype = ctypes.c_int
+        L.mla_decode_quantize_q.argtypes = [vp, vp, i64, vp]
+        L.mla_decode_quantize_q.restype = ctypes.c_int
+        L.mla_decode_reduce.argtypes = [vp, vp, vp, i32, vp, vp]
+        L.mla_decode_reduce.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _check(code: int, what: str) -> None:
+    if code != MLA_OK:
+        raise RuntimeError(f"{what} failed: {mla_status_string(code)}")
+
+
+_PLACEHOLDERS: dict = {}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if t.numel() == 0:
+        # torch gives zero-element tensors a null address; the C ABI rejects null,
+        # and a zero-element buffer is never read, so pass a small live allocation
+        ph = _PLACEHOLDERS.get(t.device)
+        if ph is None:
+            ph = _PLACEHOLDERS[t.device] = torch.zeros(16, dtype=torch.uint8, device=t.device)
+        return ph.data_ptr()
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def mla_status_string(code: int) -> str:
+    return lib().mla_status_string(int(code)).decode()
+
+
+def mla_decode_abi_version() -> int:
+    return int(lib().mla_decode_abi_version())
+
+
+def make_params(batch: int, q_dtype: str, kv_dtype: str, *, total_q: Optional[int] = None, num_units: int = 0,
+                min_chunk: int = 0, flags: int = 0, num_heads: int = 16, num_kv_heads: int = 1, qk_dim: int = 576,
+                v_dim: int = 512, page_size: int = 1) -> MlaDecodeParams:
+    return MlaDecodeParams(
+        batch=batch, total_q=batch if total_q is None else total_q, num_heads=num_heads, num_kv_heads=num_kv_heads,
+        qk_dim=qk_dim, v_dim=v_dim, page_size=page_size, q_dtype=_DTYPES.get(q_dtype, q_dtype) if isinstance(q_dtype, str) else q_dtype,
+        kv_dtype=_DTYPES.get(kv_dtype, kv_dtype) if isinstance(kv_dtype, str) else kv_dtype,
+        num_units=num_units, min_chunk=min_chunk, flags=flags,
+    )
+
+
+def mla_decode_workspace_size(params: MlaDecodeParams) -> int:
+    return int(lib().mla_decode_workspace_size(ctypes.byref(params)))
+
+
+def mla_decode_plan(params: MlaDecodeParams, workspace: torch.Tensor, stream=None) -> MlaDecodePlan:
+    plan = MlaDecodePlan()
+    code = lib().mla_decode_plan(ctypes.byref(params), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream), ctypes.byref(plan))
+    _check(code, "mla_decode_plan")
+    return plan
+
+
+def mla_decode_run(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
+                   kv_indptr: torch.Tensor, kv_indices: torch.Tensor, q_scale: Optional[torch.Tensor],
+                   kv_scale: Optional[torch.Tensor], sm_scale: float, out: torch.Tensor, stream=None) -> None:
+    for name, t in (("qo_indptr", qo_indptr), ("kv_indptr", kv_indptr), ("kv_indices", kv_indices)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16")
+    code = lib().mla_decode_run(ctypes.byref(plan), _ptr(q), _ptr(kv), _ptr(qo_indptr), _ptr(kv_indptr),
+                                _ptr(kv_indices), _ptr(q_scale), _ptr(kv_scale), float(sm_scale), _ptr(out),
+                                _stream(stream))
+    _check(code, "mla_decode_run")
+
+
+def mla_decode_quantize_q(q_bf16: torch.Tensor, q_fp8: torch.Tensor, stream=None) -> None:
+    if q_bf16.dtype != torch.bfloat16 or q_fp8.element_size() != 1 or q_fp8.numel() != q_bf16.numel():
+        raise ValueError("expected bf16 input and a 1-byte output of the same size")
+    code = lib().mla_decode_quantize_q(_ptr(q_bf16), _ptr(q_fp8), q_bf16.numel(), _stream(stream))
+    _check(code, "mla_decode_quantize_q")
+
+
+def mla_decode_reduce(part_o: torch.Tensor, part_lse: torch.Tensor, part_indptr: torch.Tensor, out: torch.Tensor,
+                      stream=None) -> None:
+    if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32 or part_indptr.dtype != torch.int32:
+        raise ValueError("partials must be float32 and part_indptr int32")
+    batch = part_indptr.numel() - 1
+    code = lib().mla_decode_reduce(_ptr(part_o), _ptr(part_lse), _ptr(part_indptr), batch, _ptr(out),
+                                   _stream(stream))
+    _check(code, "mla_decode_reduce")
+
+
+class Decoder:
+    """Owns one workspace and plan for a (batch, dtype pair); run() is one decode step."""
+
+    def __init__(self, batch: int, q_dtype: str, kv_dtype: str, device: torch.device | str = "cuda", *,
+                 num_units: int = 0, min_chunk: int = 0, flags: int = 0, stream=None):
+        self.params = make_params(batch, q_dtype, kv_dtype, num_units=num_units, min_chunk=min_chunk, flags=flags)
+        nbytes = mla_decode_workspace_size(self.params)
+        if nbytes == 0:
+            raise RuntimeError("mla_decode_workspace_size rejected the parameters")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.plan = mla_decode_plan(self.params, self.workspace, stream)
+        self.q_dtype = q_dtype
+        self.kv_dtype = kv_dtype
+
+    def run(self, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out, stream=None):
+        mla_decode_run(self.plan, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out, stream)
+        return out

@@ -1,0 +1,221 @@
+// Host side of libmla_decode: argument validation, workspace carve-up and
+// kernel launches behind the C ABI declared in include/mla_decode.h.
+//
+// Validation is pure host code and runs before any HIP call, so a rejected
+// call enqueues nothing and needs no device.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "mla_decode.h"
+#include "mla_device.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kDefaultMinChunk = 256;
+constexpr uint32_t kKnownFlags = MLA_FLAG_SEPARATE_REDUCE;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Checks every field that does not need the device.  num_units == 0 is left
+// for resolve_units().
+mla_status validate_params(const mla_decode_params* p) {
+  if (p == nullptr) return MLA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->total_q < 1 || p->num_heads < 1 || p->num_kv_heads < 1 || p->qk_dim < 1 ||
+      p->v_dim < 1 || p->page_size < 1 || p->num_units < 0 || p->min_chunk < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (p->q_dtype != MLA_DTYPE_BF16 && p->q_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_INVALID_ARG;
+  if (p->kv_dtype != MLA_DTYPE_BF16 && p->kv_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_INVALID_ARG;
+  if ((p->flags & ~kKnownFlags) != 0u) return MLA_ERR_INVALID_ARG;
+  if (p->min_chunk != 0 && p->min_chunk % mla::kSplitAlign != 0) return MLA_ERR_INVALID_ARG;
+  if (p->v_dim > p->qk_dim) return MLA_ERR_INVALID_ARG;
+  // the model constants the kernels are written for
+  if (p->num_heads != mla::kHeads || p->num_kv_heads != 1 || p->qk_dim != mla::kQKDim || p->v_dim != mla::kVDim ||
+      p->page_size != 1)
+    return MLA_ERR_UNSUPPORTED;
+  if (p->total_q != p->batch) return MLA_ERR_UNSUPPORTED;  // one decode token per sequence
+  if (p->q_dtype == MLA_DTYPE_FP8_E4M3FN && p->kv_dtype == MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (p->num_units > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+mla_status resolve_units(const mla_decode_params* p, int32_t* units, int32_t* device) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  *device = dev;
+  if (p->num_units > 0) {
+    *units = p->num_units;
+    return MLA_OK;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MLA_ERR_HIP;
+  *units = cus;
+  return MLA_OK;
+}
+
+struct Layout {
+  size_t counters, part_o, part_lse, total;
+};
+
+Layout layout_for(int32_t batch, int32_t units) {
+  Layout L;
+  L.counters = 0;
+  L.part_o = align_up((size_t)batch * sizeof(int32_t));
+  L.part_lse = L.part_o + align_up((size_t)2 * units * mla::kHeads * mla::kVDim * sizeof(float));
+  L.total = L.part_lse + align_up((size_t)2 * units * mla::kHeads * sizeof(float));
+  return L;
+}
+
+template <mla::Dt QT, mla::Dt KT>
+hipError_t launch_attention(const mla::Args& a, hipStream_t stream) {
+  hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT>), dim3(a.units), dim3(mla::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK:
+      return "MLA_OK";
+    case MLA_ERR_INVALID_ARG:
+      return "MLA_ERR_INVALID_ARG: null pointer, bad size or inconsistent parameters";
+    case MLA_ERR_UNSUPPORTED:
+      return "MLA_ERR_UNSUPPORTED: outside the shapes / dtype pairs the kernels implement";
+    case MLA_ERR_WORKSPACE:
+      return "MLA_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case MLA_ERR_HIP:
+      return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown mla_status";
+}
+
+int32_t mla_decode_abi_version(void) { return MLA_DECODE_ABI_VERSION; }
+
+size_t mla_decode_workspace_size(const mla_decode_params* params) {
+  if (validate_params(params) != MLA_OK) return 0;
+  int32_t units = params->num_units;
+  if (units == 0) {
+    int32_t device = 0;
+    if (resolve_units(params, &units, &device) != MLA_OK) return 0;
+  }
+  return layout_for(params->batch, units).total;
+}
+
+mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, mla_decode_plan_t* plan) {
+  mla_status st = validate_params(params);
+  if (st != MLA_OK) return st;
+  if (plan == nullptr) return MLA_ERR_INVALID_ARG;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MLA_ERR_WORKSPACE;
+  // the sizes that do not need the device are checked before any HIP call
+  if (params->num_units > 0 && workspace_bytes < layout_for(params->batch, params->num_units).total)
+    return MLA_ERR_WORKSPACE;
+  int32_t units = 0, device = 0;
+  st = resolve_units(params, &units, &device);
+  if (st != MLA_OK) return st;
+  const Layout L = layout_for(params->batch, units);
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+
+  mla_decode_plan_t pl;
+  memset(&pl, 0, sizeof(pl));
+  pl.params = *params;
+  pl.params.num_units = units;
+  pl.params.min_chunk = params->min_chunk > 0 ? params->min_chunk : kDefaultMinChunk;
+  pl.workspace = workspace;
+  pl.workspace_bytes = workspace_bytes;
+  pl.device = device;
+  pl.off_counters = L.counters;
+  pl.off_part_o = L.part_o;
+  pl.off_part_lse = L.part_lse;
+
+  int32_t* counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + L.counters);
+  const int nb = (params->batch + 255) / 256;
+  hipLaunchKernelGGL(mla::mla_fill_i32_kernel, dim3(nb), dim3(256), 0, stream, counters, params->batch, 0);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  *plan = pl;
+  return MLA_OK;
+}
+
+mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,
+                          const int32_t* kv_indptr, const int32_t* kv_indices, const float* q_scale,
+                          const float* kv_scale, float sm_scale, void* out, hipStream_t stream) {
+  if (plan == nullptr) return MLA_ERR_INVALID_ARG;
+  const mla_decode_params& p = plan->params;
+  mla_status st = validate_params(&p);
+  if (st != MLA_OK) return st;
+  if (p.num_units < 1 || p.min_chunk < mla::kSplitAlign) return MLA_ERR_INVALID_ARG;
+  if (plan->workspace == nullptr || plan->workspace_bytes < layout_for(p.batch, p.num_units).total)
+    return MLA_ERR_WORKSPACE;
+  if (q == nullptr || kv == nullptr || qo_indptr == nullptr || kv_indptr == nullptr || kv_indices == nullptr ||
+      out == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (p.q_dtype == MLA_DTYPE_FP8_E4M3FN && q_scale == nullptr) return MLA_ERR_INVALID_ARG;
+  if (p.kv_dtype == MLA_DTYPE_FP8_E4M3FN && kv_scale == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return MLA_ERR_INVALID_ARG;
+
+  uint8_t* ws = static_cast<uint8_t*>(plan->workspace);
+  mla::Args a;
+  a.q = q;
+  a.kv = kv;
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.q_scale = q_scale;
+  a.kv_scale = kv_scale;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + plan->off_part_lse);
+  a.counters = reinterpret_cast<int32_t*>(ws + plan->off_counters);
+  a.batch = p.batch;
+  a.units = p.num_units;
+  a.min_chunk = p.min_chunk;
+  a.fused = (p.flags & MLA_FLAG_SEPARATE_REDUCE) ? 0 : 1;
+
+  hipError_t err;
+  if (p.q_dtype == MLA_DTYPE_BF16 && p.kv_dtype == MLA_DTYPE_BF16)
+    err = launch_attention<mla::Dt::BF16, mla::Dt::BF16>(a, stream);
+  else if (p.q_dtype == MLA_DTYPE_BF16)
+    err = launch_attention<mla::Dt::BF16, mla::Dt::FP8>(a, stream);
+  else
+    err = launch_attention<mla::Dt::FP8, mla::Dt::FP8>(a, stream);
+  if (err != hipSuccess) return MLA_ERR_HIP;
+  if (!a.fused) {
+    hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(p.batch), dim3(mla::kThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+mla_status mla_decode_quantize_q(const void* q_bf16, void* q_fp8, int64_t n, hipStream_t stream) {
+  if (n < 0) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (q_bf16 == nullptr || q_fp8 == nullptr) return MLA_ERR_INVALID_ARG;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(q_bf16), s1 = s0 + (uintptr_t)n * 2;
+  const uintptr_t d0 = reinterpret_cast<uintptr_t>(q_fp8), d1 = d0 + (uintptr_t)n;
+  if (s0 < d1 && d0 < s1) return MLA_ERR_INVALID_ARG;
+  int64_t blocks = (n + 256 * 8 - 1) / (256 * 8);
+  if (blocks > 65535) blocks = 65535;
+  hipLaunchKernelGGL(mla::mla_quantize_q_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q_bf16), static_cast<uint8_t*>(q_fp8), n);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const int32_t* part_indptr, int32_t batch,
+                             void* out, hipStream_t stream) {
+  if (batch < 1 || part_indptr == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  if (part_o == nullptr || part_lse == nullptr) return MLA_ERR_INVALID_ARG;
+  if (batch > (1 << 30)) return MLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(mla::mla_reduce_external_kernel, dim3(batch), dim3(mla::kThreads), 0, stream, part_o, part_lse,
+                     part_indptr, static_cast<uint16_t*>(out));
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

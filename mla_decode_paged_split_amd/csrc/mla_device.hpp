@@ -1,0 +1,738 @@
+// Device code for paged MLA decode on gfx950 (MI355X).
+//
+// What is computed (kernelindex amd-mixed-mla submission 689529, module
+// constants and custom_kernel; submission 690201, the stage-1 / reduce pair):
+// for each sequence b, its query token t and each of 16 heads h,
+//   s_j = sm_scale * q_scale * kv_scale * <q[t,h,:576], kv[row_j,:576]>,
+//   out[t,h,:512] = kv_scale * sum_j softmax(s)_j * kv[row_j,:512]
+// over the rows row_j = kv_indices[i], i in [kv_indptr[b], kv_indptr[b+1]).
+//
+// Work split.  The rows of all sequences, concatenated in sequence order,
+// form one row space of N rows.  It is cut into n_wg equal contiguous shares
+// of C rows (C >= min_chunk, n_wg <= units): workgroup k owns rows
+// [kC, (k+1)C).  A sequence that lies inside one share is finished by that
+// workgroup; one that crosses shares is split, each piece writes a
+// normalised float32 partial plus its log2-sum-exp, and the pieces are merged
+// (by a separate merge launch, or by the last arriving workgroup).  This
+// plays the role of the pages' metadata partitioner and persistent work list
+// (submission 598454, get_mla_metadata_v1), but is recomputed from kv_indptr
+// inside every launch, so nothing has to be rebuilt when lengths change.
+//
+// Inside a workgroup a piece is walked in tiles of 64 KV rows; wave w owns
+// rows 16w..16w+15 of each tile.  Per tile a wave
+//   1. has the 16 rows in VGPRs already: they were gathered through
+//      kv_indices with 16-byte loads kDepth tiles earlier (a register ring,
+//      so kDepth tiles per wave are in flight while it computes);
+//   2. computes S^T = K . Q^T for its 16 rows with 16x16x32 MFMAs straight
+//      from those registers (K rows on the M side, the 16 heads on the N
+//      side, so every lane ends up owning one head) and copies the 512 V
+//      bytes of each row into the shared LDS tile;
+//   3. publishes its per-head tile max; after a barrier every wave applies the
+//      same running max (log2 domain; the accumulator is rescaled only when
+//      the max grows by more than 2^8), turns its scores into bf16 weights P
+//      and publishes them;
+//   4. after a second barrier computes O^T += V^T . P^T for its own 128 of the
+//      512 output columns over all 64 rows.  V's rows must sit along the MFMA
+//      K axis, so each lane reads 8-byte runs of 8 rows from LDS and
+//      interleaves them with v_perm while widening fp8 to bf16 (exact).
+// The waves own disjoint output columns, so finishing a piece only needs the
+// per-head row sums of the 4 waves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mla {
+
+constexpr int kHeads = 16;
+constexpr int kQKDim = 576;
+constexpr int kVDim = 512;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileRows = 64;             // KV rows per workgroup tile: 16 per wave
+constexpr int kColsPerWave = kVDim / kWaves;  // 128 output columns per wave
+constexpr int kSplitAlign = 32;           // share sizes are multiples of this
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;     // log2 growth of the running max tolerated before rescaling
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+enum class Dt : int { BF16 = 0, FP8 = 1 };
+
+template <Dt KV>
+struct KvLayout;
+
+// fp8 rows: 576 bytes = 36 chunks of 16 bytes.  Lane (r, g) of a wave
+// (r = lane % 16 its row, g = lane / 16) holds chunks 4j+g, j < 9, of row r;
+// chunks j < 8 are the V part.
+template <>
+struct KvLayout<Dt::FP8> {
+  static constexpr int kRowBytes = 576;
+  static constexpr int kChunks = 9;
+  static constexpr int kVChunks = 8;
+  static constexpr int kVPitch = 544;  // LDS bytes per V row: 136 dwords, rows 4 apart land 32 banks apart
+  static constexpr int kDepth = 3;     // tiles in flight per wave
+};
+
+// bf16 rows: 1152 bytes = 72 chunks; 18 per lane, 16 of them V.
+template <>
+struct KvLayout<Dt::BF16> {
+  static constexpr int kRowBytes = 1152;
+  static constexpr int kChunks = 18;
+  static constexpr int kVChunks = 16;
+  static constexpr int kVPitch = 1056;
+  static constexpr int kDepth = 2;
+};
+
+struct MergeSmem {
+  float w[64][kHeads];  // weights of the current chunk of pieces
+  float red[kWaves][kHeads];
+  float M[kHeads];
+  float inv[kHeads];
+};
+
+template <Dt KV>
+struct alignas(16) Smem {
+  union {
+    uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];  // V part of the current / next tile
+    MergeSmem merge;
+  };
+  u32x2_t p[2][kWaves][64];   // bf16 weights: wave, lane -> 4 rows of one head
+  float mx[2][kWaves][kHeads];  // per-wave tile max of each head
+  float lsum[kWaves][kHeads];
+  int bmin;
+  int bmax;
+  int arrive;
+};
+
+struct Args {
+  const void* q;
+  const void* kv;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const float* q_scale;
+  const float* kv_scale;
+  float sm_scale;
+  uint16_t* out;      // bf16 bits [total_q, 16, 512]
+  float* part_o;      // [2*units, 16, 512]
+  float* part_lse;    // [2*units, 16], log2 domain
+  int32_t* counters;  // [batch]
+  int32_t batch;
+  int32_t units;
+  int32_t min_chunk;
+  int32_t fused;
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two fp8 e4m3fn values (the low or the high 16 bits of `w`) -> two bf16,
+// exact.  With a unit scale the scaled conversion is a plain widening.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight fp8 values (two dwords, byte k = element k) -> bf16x8.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t d0, uint32_t d1) {
+  u32x4_t r;
+  r[0] = fp8x2_to_bf16x2(d0, false);
+  r[1] = fp8x2_to_bf16x2(d0, true);
+  r[2] = fp8x2_to_bf16x2(d1, false);
+  r[3] = fp8x2_to_bf16x2(d1, true);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Orders this wave's LDS stores before its later LDS loads of other lanes'
+// data (a wave executes its LDS operations in order; this stops the compiler
+// from moving them).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- partition
+
+struct Geo {
+  int32_t base;   // kv_indptr[0]
+  int32_t total;  // N rows over all sequences
+  int32_t chunk;  // C rows per workgroup share
+  int32_t n_wg;   // shares in use (>= 1)
+};
+
+__device__ __forceinline__ Geo make_geo(const int32_t* kv_indptr, int batch, int units, int min_chunk) {
+  Geo g;
+  g.base = kv_indptr[0];
+  g.total = kv_indptr[batch] - g.base;
+  int64_t c = ((int64_t)g.total + units - 1) / units;
+  c = (c + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+  if (c < min_chunk) c = min_chunk;
+  g.chunk = (int32_t)c;
+  int64_t n = ((int64_t)g.total + c - 1) / c;
+  g.n_wg = n < 1 ? 1 : (int32_t)n;
+  return g;
+}
+
+// Partial slot of the i-th piece of a sequence occupying row-space [st, en)
+// (en > st).  Workgroup k writes the piece of its first sequence to slot 2k
+// and the piece of its last sequence to slot 2k+1; a sequence that starts
+// exactly at a share boundary is the first sequence of that share.
+__device__ __forceinline__ int piece_slot(int st, int chunk, int i) {
+  const int k1 = st / chunk;
+  return i == 0 ? 2 * k1 + (st != k1 * chunk ? 1 : 0) : 2 * (k1 + i);
+}
+
+__device__ __forceinline__ int piece_count(int st, int en, int chunk) {
+  return (en - 1) / chunk - st / chunk + 1;
+}
+
+// ------------------------------------------------------------------- merge
+
+
+// Merge S partials of one query row into bf16 out_row[16][512]:
+//   out[h,:] = sum_i 2^(lse_i[h] - M[h]) o_i[h,:] / sum_i 2^(lse_i[h] - M[h]),
+// M[h] = max_i lse_i[h].  lse values are multiplied by lse_mul to bring them
+// to the log2 domain.  All 256 threads take part and every load of a pass is
+// independent of the others, so the pass costs a few memory round trips
+// rather than one per piece and head.  Thread t owns the float4 columns
+// t + 256 v (v < 8) of the flattened [16][512] row.
+template <class SlotFn>
+__device__ void merge_pieces(const float* __restrict__ part_o, const float* __restrict__ part_lse, int S,
+                             SlotFn slot_of, float lse_mul, uint16_t* __restrict__ out_row, MergeSmem& ms) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = tid & 15;
+  const int r = tid >> 4;  // 0..15
+
+  // pass 1: per-head max over all pieces (wavefront shuffles, then across waves)
+  float M = -INFINITY;
+  for (int i = r; i < S; i += 16) M = fmaxf(M, part_lse[slot_of(i) * kHeads + h] * lse_mul);
+  M = fmaxf(M, __shfl_xor(M, 16));
+  M = fmaxf(M, __shfl_xor(M, 32));
+  if (lane < 16) ms.red[w][h] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(ms.red[0][h], ms.red[1][h]), fmaxf(ms.red[2][h], ms.red[3][h]));
+  if (tid < kHeads) ms.M[tid] = M;
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float wpart = 0.f;
+  for (int i0 = 0; i0 < S; i0 += 64) {
+    const int n = min(64, S - i0);
+    __syncthreads();  // the previous chunk's weights are no longer read
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = r + 16 * k;
+      if (i < n) {
+        const float v = part_lse[slot_of(i0 + i) * kHeads + h] * lse_mul;
+        const float wt = (v == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(v - M);
+        ms.w[i][h] = wt;
+        wpart += wt;
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < n; ++i) {
+      const f32x4_t* base = reinterpret_cast<const f32x4_t*>(part_o + (size_t)slot_of(i0 + i) * kHeads * kVDim);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int f = tid + 256 * v;
+        acc[v] += ms.w[i][f >> 7] * base[f];
+      }
+    }
+  }
+  // per-head weight sums: 16 threads share a head (lanes l, l^16, l^32, l^48 of each wave)
+  wpart += __shfl_xor(wpart, 16);
+  wpart += __shfl_xor(wpart, 32);
+  __syncthreads();
+  if (lane < 16) ms.red[w][h] = wpart;
+  __syncthreads();
+  if (tid < kHeads) {
+    const float wsum = ms.red[0][tid] + ms.red[1][tid] + ms.red[2][tid] + ms.red[3][tid];
+    ms.inv[tid] = wsum > 0.f ? 1.0f / wsum : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int f = tid + 256 * v;
+    const float inv = ms.inv[f >> 7];
+    u32x2_t pk;
+    pk[0] = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
+    pk[1] = pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv);
+    *reinterpret_cast<u32x2_t*>(out_row + f * 4) = pk;
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------- zero output
+
+__device__ __forceinline__ void zero_row_by_thread(uint16_t* out_row) {
+  u32x4_t z = {0u, 0u, 0u, 0u};
+  u32x4_t* p = reinterpret_cast<u32x4_t*>(out_row);
+  for (int i = 0; i < kHeads * kVDim * 2 / 16; ++i) p[i] = z;
+}
+
+// --------------------------------------------------------------- one piece
+
+// Attention of one query row over the index positions [ip0, ip1) (one piece
+// of one sequence).  All 256 threads take part; the workgroup writes either
+// the final bf16 row (complete) or the float32 partial in `slot`.
+template <Dt QT, Dt KT>
+__device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip1, bool complete, int slot,
+                             float c_score, float out_mul) {
+  using L = KvLayout<KT>;
+  constexpr int D = L::kDepth;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+
+  // Q as the B operand of S^T = K . Q^T (lane holds head c16).  A k-step takes
+  // 8 values per lane; for fp8 KV a 16-byte chunk feeds two k-steps, for bf16
+  // KV one.  Q is read with the same d mapping as the K chunks.
+  constexpr int kSteps = kQKDim / 32;  // 18
+  bf16x8_t qb[QT == Dt::BF16 ? kSteps : 1];
+  uint64_t q8[QT == Dt::FP8 ? kSteps : 1];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int d0 = (KT == Dt::FP8) ? (((s >> 1) * 4 + g) * 16 + (s & 1) * 8) : ((s * 4 + g) * 8);
+    if constexpr (QT == Dt::BF16) {
+      qb[s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                 ((size_t)t * kHeads + c16) * kQKDim + d0);
+    } else {
+      q8[s] = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) +
+                                                 ((size_t)t * kHeads + c16) * kQKDim + d0);
+    }
+  }
+
+  const int T = (ip1 - ip0 + kTileRows - 1) / kTileRows;
+  const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
+
+  // register ring: tile t lives in slot t % D
+  u32x4_t dat[D][L::kChunks];
+  int idxn[D];
+  auto row_index = [&](int tt) {
+    const int pos = ip0 + tt * kTileRows + my_row;
+    return a.kv_indices[pos < ip1 ? pos : ip0];
+  };
+  auto load_tile = [&](u32x4_t(&dst)[L::kChunks], int idx) {
+    const uint8_t* row = kvb + (size_t)idx * L::kRowBytes + g * 16;
+#pragma unroll
+    for (int j = 0; j < L::kChunks; ++j) dst[j] = *reinterpret_cast<const u32x4_t*>(row + j * 64);
+  };
+  // Prologue in the steady state's load order (tile k's rows, then the index
+  // for tile k + D), kept by scheduling barriers: the loop's wait counts are
+  // computed over both the prologue and the loop back edge.
+  int idx0[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) idx0[k] = row_index(k);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    load_tile(dat[k], idx0[k]);
+    __builtin_amdgcn_sched_barrier(0);
+    idxn[k] = row_index(k + D);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int jb = 0; jb < 8; ++jb) acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // O^T += V^T . P^T over the 64 rows of tile `tt`, this wave's 128 columns.
+  // k-step ks covers rows 32ks..32ks+31; slot s of lane group g is row
+  // R = 32ks + (s/4)*16 + g*4 + s%4, which is wave 2ks + s/4's row g*4 + s%4.
+  // Block jb holds columns 128w + m*8 + jb, m = 0..15; lane c16 feeds m = c16.
+  auto pv = [&](int tt) {
+    const int buf = tt & 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4_t pp;
+      const u32x2_t p0 = sm.p[buf][2 * ks][lane];
+      const u32x2_t p1 = sm.p[buf][2 * ks + 1][lane];
+      pp[0] = p0[0];
+      pp[1] = p0[1];
+      pp[2] = p1[0];
+      pp[3] = p1[1];
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pp);
+      if constexpr (KT == Dt::FP8) {
+        u32x2_t rv[8];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int R = 32 * ks + (sl >> 2) * 16 + g * 4 + (sl & 3);
+          rv[sl] = *reinterpret_cast<const u32x2_t*>(&sm.v[buf][R][kColsPerWave * w + c16 * 8]);
+        }
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd) {
+          u32x4_t op[4];
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const uint32_t A = rv[2 * pr][wd];
+            const uint32_t B = rv[2 * pr + 1][wd];
+            const uint32_t lo = __builtin_amdgcn_perm(A, B, 0x01050004u);  // A.b0 B.b0 A.b1 B.b1
+            const uint32_t hi = __builtin_amdgcn_perm(A, B, 0x03070206u);  // A.b2 B.b2 A.b3 B.b3
+            op[0][pr] = fp8x2_to_bf16x2(lo, false);
+            op[1][pr] = fp8x2_to_bf16x2(lo, true);
+            op[2][pr] = fp8x2_to_bf16x2(hi, false);
+            op[3][pr] = fp8x2_to_bf16x2(hi, true);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int jb = wd * 4 + u;
+            acc[jb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op[u]), pop, acc[jb], 0, 0, 0);
+          }
+        }
+      } else {
+        u32x4_t rv[8];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int R = 32 * ks + (sl >> 2) * 16 + g * 4 + (sl & 3);
+          rv[sl] = *reinterpret_cast<const u32x4_t*>(&sm.v[buf][R][(kColsPerWave * w + c16 * 8) * 2]);
+        }
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) {
+          const uint32_t sel = (jb & 1) ? 0x03020706u : 0x01000504u;
+          u32x4_t op;
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr)
+            op[pr] = __builtin_amdgcn_perm(rv[2 * pr][jb >> 1], rv[2 * pr + 1][jb >> 1], sel);
+          acc[jb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op), pop, acc[jb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // One tile: `kc` is the ring slot (a compile-time constant), `refill` says
+  // whether to start the loads of tile tt + D into the slot just consumed.
+  // P.V runs one tile behind S^T, so the MFMA / conversion work of both sits
+  // between the same two barriers; the weights of tile tt are made with the
+  // running max known before it and kept unless some score of the tile exceeds
+  // that max by more than the slack (then every wave rescales and redoes them).
+  auto step = [&](auto kc, int tt, auto refill) {
+    constexpr int k = decltype(kc)::value;
+    const int buf = tt & 1;
+    // ---- S^T for this wave's 16 rows (two accumulation chains); V part to LDS
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t s1 = {0.f, 0.f, 0.f, 0.f};
+    uint8_t* vrow = &sm.v[buf][16 * w + c16][0];
+#pragma unroll
+    for (int j = 0; j < L::kChunks; ++j) {
+      const u32x4_t kk = dat[k][j];
+      if (j < L::kVChunks) *reinterpret_cast<u32x4_t*>(vrow + (j * 4 + g) * 16) = kk;
+      if constexpr (KT == Dt::BF16) {
+        if (j & 1)
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk), qb[j], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk), qb[j], s0, 0, 0, 0);
+      } else if constexpr (QT == Dt::BF16) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kk[0], kk[1]), qb[2 * j], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kk[2], kk[3]), qb[2 * j + 1], s1, 0, 0, 0);
+      } else {
+        const uint64_t k0 = (uint64_t)kk[0] | ((uint64_t)kk[1] << 32);
+        const uint64_t k1 = (uint64_t)kk[2] | ((uint64_t)kk[3] << 32);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k0, (long)q8[2 * j], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k1, (long)q8[2 * j + 1], s1, 0, 0, 0);
+      }
+    }
+    // ---- refill this ring slot with tile tt + D, fetch the index of tile tt + 2D.
+    // Issued unconditionally in the steady-state loop (indices past the piece
+    // clamp to its first row), so every trip issues the same loads and the
+    // compiler's wait counts stay exact: the ring really keeps D tiles in flight.
+    if constexpr (decltype(refill)::value) {
+      load_tile(dat[k], idxn[k]);
+      idxn[k] = row_index(tt + 2 * D);
+    }
+    // ---- previous tile's P.V (its weights and V were published before the last barrier)
+    if (tt > 0) pv(tt - 1);
+    // ---- scores (log2 domain), masked past the piece end
+    const f32x4_t sc = s0 + s1;
+    float x[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = ip0 + tt * kTileRows + 16 * w + g * 4 + i;
+      x[i] = (pos < ip1) ? sc[i] * c_score : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) sm.mx[buf][w][c16] = mx;
+    // ---- speculative weights with the running max known so far
+    auto make_p = [&](u32x2_t& pw) {
+      float pv4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv4[i] = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
+      pw[0] = pack_bf16x2(pv4[0], pv4[1]);
+      pw[1] = pack_bf16x2(pv4[2], pv4[3]);
+      sm.p[buf][w][lane] = pw;
+    };
+    u32x2_t pw;
+    make_p(pw);
+    __syncthreads();
+    // ---- every wave sees the same four maxima, so the decision is workgroup-uniform
+    const float mt =
+        fmaxf(fmaxf(sm.mx[buf][0][c16], sm.mx[buf][1][c16]), fmaxf(sm.mx[buf][2][c16], sm.mx[buf][3][c16]));
+    const bool need = mt > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) acc[jb] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      make_p(pw);  // nobody reads tile tt's weights before the next step
+      __syncthreads();
+    }
+    // the row sum uses the same bf16-rounded weights the P.V product sees
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      l_run += __builtin_bit_cast(float, pw[i] << 16) + __builtin_bit_cast(float, pw[i] & 0xFFFF0000u);
+  };
+
+  int t0 = 0;
+  for (; t0 + D <= T; t0 += D) {
+    step(std::integral_constant<int, 0>{}, t0, std::true_type{});
+    if constexpr (D > 1) step(std::integral_constant<int, 1>{}, t0 + 1, std::true_type{});
+    if constexpr (D > 2) step(std::integral_constant<int, 2>{}, t0 + 2, std::true_type{});
+    if constexpr (D > 3) step(std::integral_constant<int, 3>{}, t0 + 3, std::true_type{});
+  }
+  // the last T mod D tiles are already in the ring
+  if (t0 < T) step(std::integral_constant<int, 0>{}, t0, std::false_type{});
+  if constexpr (D > 1)
+    if (t0 + 1 < T) step(std::integral_constant<int, 1>{}, t0 + 1, std::false_type{});
+  if constexpr (D > 2)
+    if (t0 + 2 < T) step(std::integral_constant<int, 2>{}, t0 + 2, std::false_type{});
+  static_assert(D <= 4, "ring depth above 4 needs more unrolled steps");
+  pv(T - 1);
+
+  // ---- finish: per-head row sums of the 4 waves, then this wave's 128 columns
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (g == 0) sm.lsum[w][c16] = l_tot;
+  __syncthreads();
+  const float Lsum = sm.lsum[0][c16] + sm.lsum[1][c16] + sm.lsum[2][c16] + sm.lsum[3][c16];
+  const float scale = Lsum > 0.f ? out_mul / Lsum : 0.f;
+  // lane (c16, g) holds, for block jb and i < 4, head c16 at column 128w + (4g+i)*8 + jb
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int col = kColsPerWave * w + (4 * g + i) * 8;
+    if (complete) {
+      u32x4_t pk;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(acc[2 * u][i] * scale, acc[2 * u + 1][i] * scale);
+      *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
+    } else {
+      f32x4_t v0, v1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v0[u] = acc[u][i] * scale;
+        v1[u] = acc[4 + u][i] * scale;
+      }
+      f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)slot * kHeads + c16) * kVDim + col);
+      dst[0] = v0;
+      dst[1] = v1;
+    }
+  }
+  if (!complete && w == 0 && g == 0)
+    a.part_lse[slot * kHeads + c16] = Lsum > 0.f ? m_run + fast_log2(Lsum) : -INFINITY;
+  __syncthreads();  // the shared tile and sums may be reused by the next piece
+}
+
+// ------------------------------------------------------------------ kernels
+
+template <Dt QT, Dt KT>
+__global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
+  __shared__ Smem<KT> sm;
+  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk);
+  const int k = blockIdx.x;
+  if (k >= geo.n_wg) return;
+  const int lo = k * geo.chunk;
+  const int hi = min(lo + geo.chunk, geo.total);
+
+  const float qs = (QT == Dt::FP8) ? *a.q_scale : 1.0f;
+  const float ks = (KT == Dt::FP8) ? *a.kv_scale : 1.0f;
+  const float c_score = a.sm_scale * qs * ks * kLog2e;
+  const float out_mul = ks;
+
+  if (threadIdx.x == 0) {
+    sm.bmin = 0x7fffffff;
+    sm.bmax = -1;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.batch; j += kThreads) {
+    const int st = a.kv_indptr[j] - geo.base;
+    const int en = a.kv_indptr[j + 1] - geo.base;
+    if (en > st) {
+      if (st < hi && en > lo) {
+        atomicMin(&sm.bmin, j);
+        atomicMax(&sm.bmax, j);
+      }
+    } else {
+      // an empty sequence belongs to the share holding its position
+      int owner = st / geo.chunk;
+      if (owner > geo.n_wg - 1) owner = geo.n_wg - 1;
+      if (owner == k) zero_row_by_thread(a.out + (size_t)a.qo_indptr[j] * kHeads * kVDim);
+    }
+  }
+  __syncthreads();
+  const int bmin = sm.bmin;
+  const int bmax = sm.bmax;
+
+  for (int b = bmin; b <= bmax; ++b) {
+    const int st = a.kv_indptr[b] - geo.base;
+    const int en = a.kv_indptr[b + 1] - geo.base;
+    if (en <= st) continue;
+    const int s_lo = max(st, lo);
+    const int s_hi = min(en, hi);
+    const bool complete = (st >= lo) && (en <= hi);
+    const int slot = complete ? -1 : (st <= lo ? 2 * k : 2 * k + 1);
+    const int t = a.qo_indptr[b];
+    attend_piece<QT, KT>(a, sm, t, s_lo + geo.base, s_hi + geo.base, complete, slot, c_score, out_mul);
+    if (!complete && a.fused) {
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) sm.arrive = atomicAdd(&a.counters[b], 1);
+      __syncthreads();
+      const int S = piece_count(st, en, geo.chunk);
+      if (sm.arrive == S - 1) {
+        __threadfence();
+        const int chunk = geo.chunk;
+        merge_pieces(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f,
+                     a.out + (size_t)t * kHeads * kVDim, sm.merge);
+        if (threadIdx.x == 0) atomicExch(&a.counters[b], 0);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Separate merge launch: one workgroup per sequence; sequences that were not
+// split were finished by the attention kernel and are skipped.
+__global__ __launch_bounds__(kThreads) void mla_merge_split_kernel(Args a) {
+  const int b = blockIdx.x;
+  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk);
+  const int st = a.kv_indptr[b] - geo.base;
+  const int en = a.kv_indptr[b + 1] - geo.base;
+  if (en <= st) return;
+  const int S = piece_count(st, en, geo.chunk);
+  if (S <= 1) return;
+  const int chunk = geo.chunk;
+  __shared__ MergeSmem ms;
+  merge_pieces(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f,
+               a.out + (size_t)a.qo_indptr[b] * kHeads * kVDim, ms);
+}
+
+// Merge of caller-provided partials (natural-log lse), one workgroup per sequence.
+__global__ __launch_bounds__(kThreads) void mla_reduce_external_kernel(const float* part_o, const float* part_lse,
+                                                                       const int32_t* part_indptr, uint16_t* out) {
+  const int b = blockIdx.x;
+  const int p0 = part_indptr[b];
+  const int S = part_indptr[b + 1] - p0;
+  uint16_t* out_row = out + (size_t)b * kHeads * kVDim;
+  if (S <= 0) {
+    // no parts: zeros, written cooperatively
+    u32x4_t z = {0u, 0u, 0u, 0u};
+    u32x4_t* p = reinterpret_cast<u32x4_t*>(out_row);
+    for (int i = threadIdx.x; i < kHeads * kVDim * 2 / 16; i += kThreads) p[i] = z;
+    return;
+  }
+  __shared__ MergeSmem ms;
+  merge_pieces(part_o, part_lse, S, [=](int i) { return p0 + i; }, kLog2e, out_row, ms);
+}
+
+__global__ void mla_fill_i32_kernel(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------ step a0: Q cast
+
+// bf16 -> fp8 e4m3fn, round to nearest even, non-saturating (magnitudes above
+// 464, infinities and NaN give the NaN code with the input's sign).  Integer
+// arithmetic on the bit fields, so the result does not depend on any
+// hardware conversion mode.
+__device__ __forceinline__ uint32_t bf16_to_e4m3fn(uint32_t x) {
+  const uint32_t sign = (x >> 8) & 0x80u;
+  const int e = (int)((x >> 7) & 0xFFu);
+  const uint32_t m = x & 0x7Fu;
+  if (e == 0xFF) return sign | 0x7Fu;
+  int E = e - 127 + 7;  // e4m3 biased exponent
+  if (E >= 1) {
+    uint32_t m3 = m >> 4;
+    const uint32_t rem = m & 0xFu;
+    if (rem > 8u || (rem == 8u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) {
+      m3 = 0;
+      ++E;
+    }
+    if (E > 15 || (E == 15 && m3 == 7u)) return sign | 0x7Fu;
+    return sign | ((uint32_t)E << 3) | m3;
+  }
+  // below 2^-6: units of 2^-9 (the e4m3 subnormal step)
+  const int shift = 125 - e;  // significand (with hidden bit) is 8 bits wide
+  if (e == 0 || shift > 9) return sign;  // bf16 subnormals and anything below 2^-10 round to zero
+  const uint32_t sig = 0x80u | m;
+  uint32_t n = sig >> shift;
+  const uint32_t rem = sig & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (n & 1u))) ++n;
+  return sign | n;  // n == 8 is the smallest normal, encoded the same way
+}
+
+__global__ void mla_quantize_q_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n; i += stride) {
+    if (i + 8 <= n && ((reinterpret_cast<uintptr_t>(src + i) & 15u) == 0) && ((reinterpret_cast<uintptr_t>(dst + i) & 7u) == 0)) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + i);
+      u32x2_t o;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t a0 = bf16_to_e4m3fn(v[2 * k] & 0xFFFFu);
+        const uint32_t a1 = bf16_to_e4m3fn(v[2 * k] >> 16);
+        const uint32_t a2 = bf16_to_e4m3fn(v[2 * k + 1] & 0xFFFFu);
+        const uint32_t a3 = bf16_to_e4m3fn(v[2 * k + 1] >> 16);
+        o[k] = a0 | (a1 << 8) | (a2 << 16) | (a3 << 24);
+      }
+      *reinterpret_cast<u32x2_t*>(dst + i) = o;
+    } else {
+      for (int64_t j = i; j < n && j < i + 8; ++j) dst[j] = (uint8_t)bf16_to_e4m3fn(src[j]);
+    }
+  }
+}
+
+}  // namespace mla

@@ -1,0 +1,169 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from mla_decode_paged_split_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["mla_decode_workspace_size", "mla_decode_plan", "mla_decode_run", "mla_decode_quantize_q",
+              "mla_decode_reduce", "mla_status_string", "mla_decode_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.library_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header():
+    # 12 int32 fields; the plan carries params + pointer + size + 2 int32 + 3 offsets
+    assert ctypes.sizeof(B.MlaDecodeParams) == 48
+    assert ctypes.sizeof(B.MlaDecodePlan) == 48 + 8 + 8 + 8 + 24
+
+
+def test_abi_version_and_status_strings():
+    assert B.mla_decode_abi_version() == 1
+    for code in range(5):
+        s = B.mla_status_string(code)
+        assert s.startswith("MLA_")
+    assert "unknown" in B.mla_status_string(99)
+
+
+def _params(**kw):
+    base = dict(batch=4, q_dtype="bf16", kv_dtype="fp8", num_units=256)
+    base.update(kw)
+    return B.make_params(**base)
+
+
+def test_workspace_size_is_host_arithmetic():
+    p = _params(batch=64, num_units=256)
+    n = B.mla_decode_workspace_size(p)
+    # counters (64 int32, padded to 256 B) + partial O (2*256*16*512 fp32) + partial lse (2*256*16 fp32)
+    assert n == 256 + 2 * 256 * 16 * 512 * 4 + 2 * 256 * 16 * 4
+    assert B.mla_decode_workspace_size(_params(batch=1000, num_units=4)) == 4096 + 2 * 4 * 16 * 512 * 4 + 512
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(batch=0), B.MLA_ERR_INVALID_ARG),
+        (dict(total_q=0), B.MLA_ERR_INVALID_ARG),
+        (dict(num_units=-1), B.MLA_ERR_INVALID_ARG),
+        (dict(min_chunk=33), B.MLA_ERR_INVALID_ARG),
+        (dict(min_chunk=-32), B.MLA_ERR_INVALID_ARG),
+        (dict(flags=8), B.MLA_ERR_INVALID_ARG),
+        (dict(q_dtype=7), B.MLA_ERR_INVALID_ARG),
+        (dict(num_heads=8), B.MLA_ERR_UNSUPPORTED),
+        (dict(num_kv_heads=2), B.MLA_ERR_UNSUPPORTED),
+        (dict(qk_dim=512, v_dim=512), B.MLA_ERR_UNSUPPORTED),
+        (dict(v_dim=128), B.MLA_ERR_UNSUPPORTED),
+        (dict(page_size=16), B.MLA_ERR_UNSUPPORTED),
+        (dict(total_q=8), B.MLA_ERR_UNSUPPORTED),
+        (dict(q_dtype="fp8", kv_dtype="bf16"), B.MLA_ERR_UNSUPPORTED),
+    ],
+)
+def test_plan_rejects_bad_params_before_any_hip_call(kw, code):
+    p = _params(**kw)
+    plan = B.MlaDecodePlan()
+    got = B.lib().mla_decode_plan(ctypes.byref(p), 4096, 1 << 30, None, ctypes.byref(plan))
+    assert got == code
+    assert B.mla_decode_workspace_size(p) == 0
+
+
+def test_plan_workspace_checks():
+    p = _params()
+    plan = B.MlaDecodePlan()
+    L = B.lib()
+    assert L.mla_decode_plan(ctypes.byref(p), None, 1 << 30, None, ctypes.byref(plan)) == B.MLA_ERR_WORKSPACE
+    assert L.mla_decode_plan(ctypes.byref(p), 4096 + 8, 1 << 30, None, ctypes.byref(plan)) == B.MLA_ERR_WORKSPACE
+    assert L.mla_decode_plan(ctypes.byref(p), 4096, 100, None, ctypes.byref(plan)) == B.MLA_ERR_WORKSPACE
+    assert L.mla_decode_plan(ctypes.byref(p), 4096, 1 << 30, None, None) == B.MLA_ERR_INVALID_ARG
+
+
+def _fake_plan(**kw):
+    p = _params(**kw)
+    plan = B.MlaDecodePlan()
+    plan.params = p
+    plan.params.min_chunk = 256
+    plan.workspace = 4096
+    plan.workspace_bytes = B.mla_decode_workspace_size(_params())
+    return plan
+
+
+def test_run_rejects_bad_arguments_before_any_hip_call():
+    L = B.lib()
+    plan = _fake_plan()
+    ptrs = [4096] * 5
+    ok_scale = 8192
+
+    def run(pl, q=4096, kv=4096, qo=4096, kvp=4096, idx=4096, qs=None, ks=ok_scale, sm=1 / 24, out=4096):
+        return L.mla_decode_run(ctypes.byref(pl) if pl is not None else None, q, kv, qo, kvp, idx, qs, ks, sm, out,
+                                None)
+
+    assert run(None) == B.MLA_ERR_INVALID_ARG
+    assert run(plan, q=None) == B.MLA_ERR_INVALID_ARG
+    assert run(plan, kv=None) == B.MLA_ERR_INVALID_ARG
+    assert run(plan, idx=None) == B.MLA_ERR_INVALID_ARG
+    assert run(plan, out=None) == B.MLA_ERR_INVALID_ARG
+    assert run(plan, ks=None) == B.MLA_ERR_INVALID_ARG  # fp8 KV needs its scale
+    assert run(plan, sm=float("nan")) == B.MLA_ERR_INVALID_ARG
+    assert run(plan, sm=float("inf")) == B.MLA_ERR_INVALID_ARG
+    a8 = _fake_plan(q_dtype="fp8")
+    assert run(a8) == B.MLA_ERR_INVALID_ARG  # fp8 Q needs its scale
+    small = _fake_plan()
+    small.workspace_bytes = 100
+    assert run(small) == B.MLA_ERR_WORKSPACE
+    nows = _fake_plan()
+    nows.workspace = None
+    assert run(nows) == B.MLA_ERR_WORKSPACE
+    bad = _fake_plan(num_heads=32)
+    assert run(bad) == B.MLA_ERR_UNSUPPORTED
+    unresolved = _fake_plan()
+    unresolved.params.min_chunk = 0
+    assert run(unresolved) == B.MLA_ERR_INVALID_ARG
+    del ptrs
+
+
+def test_quantize_and_reduce_argument_checks():
+    L = B.lib()
+    assert L.mla_decode_quantize_q(4096, 1 << 20, -1, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_quantize_q(None, None, 0, None) == B.MLA_OK  # nothing to do, nothing enqueued
+    assert L.mla_decode_quantize_q(None, 4096, 10, None) == B.MLA_ERR_INVALID_ARG
+    # overlapping source and destination
+    assert L.mla_decode_quantize_q(4096, 4100, 10, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_reduce(4096, 4096, 4096, 0, 4096, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_reduce(None, 4096, 4096, 2, 4096, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_reduce(4096, 4096, None, 2, 4096, None) == B.MLA_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_auto_units_without_a_device_reports_hip_error():
+    p = _params(num_units=0)
+    assert B.mla_decode_workspace_size(p) == 0
+    plan = B.MlaDecodePlan()
+    assert B.lib().mla_decode_plan(ctypes.byref(p), 4096, 1 << 30, None, ctypes.byref(plan)) == B.MLA_ERR_HIP
+
+
+def test_binding_has_no_cpu_fallback():
+    # the product path refuses host tensors instead of computing on the CPU
+    with pytest.raises(ValueError):
+        B._ptr(torch.zeros(4))

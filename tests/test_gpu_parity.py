@@ -1,0 +1,206 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small cases span several 32-row tiles with ragged tails, every dtype pair,
+and work splits from one workgroup per sequence down to 32-row shares (more
+than 64 pieces per sequence).  Invariants that need no oracle are checked too:
+split count, pool permutation, determinism, empty sequences, closed forms.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_decode_paged_split_amd import binding, synth
+
+from mla_cases import DevCase, Timer, assert_parity, log, oracle_ref, to64
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8")]
+LENGTHS = [1, 2, 31, 32, 33, 64, 100, 257, 513, 1000, 2053]
+# (num_units, min_chunk, flags): one share for everything, a few shares, many
+# shares, and 32-row shares (up to 65 pieces for the 2053-row sequence)
+SPLITS = [(1, 32, 0), (8, 32, 0), (8, 32, 1), (256, 32, 0), (4096, 32, 0), (4096, 32, 1)]
+
+
+def test_device_facts(gpu):
+    p = torch.cuda.get_device_properties(0)
+    log(f"  device={p.name} gcn={getattr(p, 'gcnArchName', '?')} CUs={p.multi_processor_count} "
+        f"mem={p.total_memory / 2**30:.0f}GiB")
+    assert "gfx950" in getattr(p, "gcnArchName", "gfx950")
+
+
+def test_quantize_q_exhaustive_bit_exact(gpu):
+    codes = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16)
+    src = codes.view(torch.bfloat16).to(gpu)
+    dst = torch.empty(1 << 16, dtype=torch.uint8, device=gpu)
+    binding.mla_decode_quantize_q(src, dst)
+    torch.cuda.synchronize()
+    expect = oracle.bf16_bits_to_fp8_bits(codes.numpy())
+    got = dst.cpu().numpy()
+    bad = np.nonzero(got != expect)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first {hex(bad[0])}: got {got[bad[0]]:#x} want {expect[bad[0]]:#x}"
+
+
+def test_quantize_q_unaligned_tail(gpu):
+    codes = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16)
+    big = codes.view(torch.bfloat16).to(gpu)
+    src = big[1:-2]  # 2-byte offset: takes the element-by-element path
+    dst_buf = torch.empty(src.numel() + 3, dtype=torch.uint8, device=gpu)
+    dst = dst_buf[3:]
+    binding.mla_decode_quantize_q(src, dst)
+    torch.cuda.synchronize()
+    expect = oracle.bf16_bits_to_fp8_bits(codes.numpy()[1:-2])
+    assert np.array_equal(dst.cpu().numpy(), expect)
+
+
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_parity_small_all_splits(gpu, qd, kd):
+    spec = synth.CaseSpec(batch=len(LENGTHS), q_dtype=qd, kv_dtype=kd, lengths=LENGTHS, permuted=True,
+                          extra_pool_rows=37, seed=100 + 10 * PAIRS.index((qd, kd)))
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    with Timer("oracle"):
+        ref = oracle_ref(case)
+    for units, chunk, flags in SPLITS:
+        log(f"[parity {qd}/{kd} units={units} min_chunk={chunk} flags={flags}]")
+        out = dc.run(num_units=units, min_chunk=chunk, flags=flags)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"{qd}/{kd} u{units} c{chunk} f{flags}")
+
+
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_split_count_invariance(gpu, qd, kd):
+    """Any split gives the unsplit result up to the bf16 rounding of the softmax weights.
+
+    The P.V product takes the weights p_i = 2^(x_i - m) rounded to bf16
+    (relative error <= 2^-9 each), and m is each piece's own running max, so
+    two splits round differently.  Elementwise the outputs can then differ by
+    at most 2^-8 * max_i |v_i - O| (two roundings of each weight) plus one bf16
+    rounding of each output (2^-9 |O|); that bound uses 2 max_i |v_i| for
+    max_i |v_i - O|.  Statistically the weight errors average out, so the
+    normwise difference must also stay below 5e-3.
+    """
+    spec = synth.CaseSpec(batch=4, q_dtype=qd, kv_dtype=kd, lengths=[4000, 129, 2049, 700], seed=300)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    vmax = np.zeros((4, 512))
+    for b in range(4):
+        rows = case.kv_indices[case.kv_indptr[b]:case.kv_indptr[b + 1]].long()
+        v = case.kv[rows, :512].float() * (case.kv_scale if case.kv_scale is not None else 1.0)
+        vmax[b] = v.abs().max(dim=0).values.double().numpy()
+    base = to64(dc.run(num_units=1, min_chunk=32))  # one workgroup, nothing split
+    for units in (2, 3, 7, 64, 1024):
+        got = to64(dc.run(num_units=units, min_chunk=32))
+        d = np.abs(got - base)
+        bound = 2.0 ** -8 * 2 * vmax[:, None, :] + 2.0 ** -8 * np.abs(base) + 1e-6
+        nrm = float(np.linalg.norm(got - base) / np.linalg.norm(base))
+        log(f"  units={units}: max|diff|={d.max():.3e} normwise={nrm:.2e} max(diff/bound)={np.max(d / bound):.3f}")
+        assert np.all(d <= bound) and nrm <= 5e-3
+
+
+def test_pool_permutation_bit_identical(gpu):
+    spec = synth.CaseSpec(batch=5, q_dtype="bf16", kv_dtype="fp8", lengths=[300, 1, 77, 1024, 45], seed=400)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    a = dc.run(num_units=16, min_chunk=64).cpu()
+    g = torch.Generator().manual_seed(401)
+    perm = torch.randperm(case.kv.shape[0], generator=g)
+    moved = torch.empty_like(case.kv.view(torch.uint8))
+    moved[perm] = case.kv.view(torch.uint8)
+    case2 = synth.Case(spec, case.q_bf16, moved.view(torch.float8_e4m3fn), case.kv_scale, case.qo_indptr,
+                       case.kv_indptr, perm[case.kv_indices.long()].to(torch.int32), case.lengths)
+    b = DevCase(case2, gpu).run(num_units=16, min_chunk=64).cpu()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_determinism(gpu, flags):
+    spec = synth.CaseSpec(batch=6, q_dtype="fp8", kv_dtype="fp8", lengths=[5000, 3, 900, 4096, 64, 1500], seed=500)
+    dc = DevCase(synth.make_case(spec), gpu)
+    dec = dc.decoder(num_units=64, min_chunk=32, flags=flags)
+    a = dc.run(dec).clone()
+    b = dc.run(dec).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_empty_sequences_give_zeros(gpu, qd, kd):
+    lens = [0, 5, 0, 0, 100, 0]
+    spec = synth.CaseSpec(batch=len(lens), q_dtype=qd, kv_dtype=kd, lengths=lens, seed=600)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units, chunk in ((1, 32), (4, 32), (64, 32)):
+        out = to64(dc.run(num_units=units, min_chunk=chunk))
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert np.array_equal(out[b], np.zeros((16, 512)))
+        assert_parity(ref, out, f"empties u{units}")
+
+
+def test_all_sequences_empty(gpu):
+    spec = synth.CaseSpec(batch=3, q_dtype="bf16", kv_dtype="fp8", lengths=[0, 0, 0], extra_pool_rows=4, seed=610)
+    out = to64(DevCase(synth.make_case(spec), gpu).run())
+    assert np.array_equal(out, np.zeros_like(out))
+
+
+def test_single_row_returns_v_exactly(gpu):
+    # bf16 KV: softmax over one row is exactly 1, so the output is V itself
+    spec = synth.CaseSpec(batch=3, q_dtype="bf16", kv_dtype="bf16", lengths=[1, 1, 1], permuted=True,
+                          extra_pool_rows=10, seed=700)
+    case = synth.make_case(spec)
+    out = DevCase(case, gpu).run().cpu()
+    rows = case.kv_indices.long()
+    expect = case.kv[rows, :512][:, None, :].expand(3, 16, 512)
+    assert torch.equal(out.view(torch.int16), expect.contiguous().view(torch.int16))
+    # fp8 KV: the output is the float32 product kv_scale * v rounded to bf16
+    spec8 = synth.CaseSpec(batch=2, q_dtype="fp8", kv_dtype="fp8", lengths=[1, 1], seed=701)
+    case8 = synth.make_case(spec8)
+    out8 = DevCase(case8, gpu).run().cpu()
+    v = case8.kv[case8.kv_indices.long(), :512].to(torch.float32) * case8.kv_scale
+    assert torch.equal(out8.view(torch.int16), v[:, None, :].expand(2, 16, 512).to(torch.bfloat16).view(torch.int16))
+
+
+def test_constant_v_returns_constant(gpu):
+    spec = synth.CaseSpec(batch=2, q_dtype="bf16", kv_dtype="bf16", lengths=[700, 2000], seed=800)
+    case = synth.make_case(spec)
+    c = torch.randn(512, generator=torch.Generator().manual_seed(801)).to(torch.bfloat16)
+    case.kv[:, :512] = c  # rope dims stay random, scores still differ
+    out = DevCase(case, gpu).run(num_units=16, min_chunk=64).cpu().float()
+    err = (out - c.float()).abs().max().item()
+    log(f"  constant V: max err {err:.3e}")
+    assert err <= float(c.float().abs().max()) * 2.0 ** -8
+
+
+def test_external_reduce_matches_merge(gpu):
+    rng = np.random.default_rng(900)
+    counts = [0, 1, 2, 5, 64, 70, 3]
+    P = sum(counts)
+    part_o = rng.standard_normal((P, 16, 512)).astype(np.float32)
+    lse = (rng.standard_normal((P, 16)) * 3).astype(np.float32)
+    lse[1, 3] = -np.inf
+    lse[rng.random((P, 16)) < 0.05] = -np.inf
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    out = torch.full((len(counts), 16, 512), float("nan"), dtype=torch.bfloat16, device=gpu)
+    binding.mla_decode_reduce(torch.from_numpy(part_o).to(gpu), torch.from_numpy(lse).to(gpu),
+                              torch.from_numpy(indptr).to(gpu), out)
+    torch.cuda.synchronize()
+    got = to64(out)
+    for b in range(len(counts)):
+        p0, p1 = indptr[b], indptr[b + 1]
+        if p1 == p0:
+            assert np.array_equal(got[b], np.zeros((16, 512)))
+            continue
+        ref = oracle.merge_partials(part_o[p0:p1].astype(np.float64), lse[p0:p1].astype(np.float64))
+        assert np.max(np.abs(got[b] - ref)) <= 2.0 ** -8 * np.max(np.abs(ref)) + 1e-6, b
+
+
+def test_lengths_change_without_replanning(gpu):
+    # the split is recomputed from kv_indptr on every run: one plan serves growing lengths
+    dec = binding.Decoder(3, "bf16", "fp8", gpu, num_units=32, min_chunk=32)
+    for step, lens in enumerate(([10, 500, 33], [11, 501, 34], [900, 1, 4000])):
+        case = synth.make_case(synth.CaseSpec(batch=3, q_dtype="bf16", kv_dtype="fp8", lengths=lens, seed=950 + step))
+        dc = DevCase(case, gpu)
+        assert_parity(oracle_ref(case), to64(dc.run(dec)), f"step{step}")
