@@ -65,9 +65,12 @@ typedef enum {
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP8_E4M3FN = 1 } mla_dtype;
 
 /* Flags for mla_decode_params.flags. */
-#define MLA_FLAG_SEPARATE_REDUCE 1u /* merge split partials in a second kernel
-                                       instead of in the last workgroup of each
-                                       split sequence */
+#define MLA_FLAG_FUSED_MERGE 1u /* merge split partials in the last arriving
+                                   workgroup of each split sequence instead of
+                                   a second launch.  Correct on any device, but
+                                   slower on MI355X: the device-scope release /
+                                   acquire it needs writes back and invalidates
+                                   the per-XCD L2 in every split workgroup. */
 
 /*
  * Problem description.  The fixed fields restate the model constants of
@@ -105,7 +108,7 @@ typedef struct {
   size_t workspace_bytes;
   int32_t device;
   int32_t reserved;
-  uint64_t off_counters; /* int32 [batch]: arrivals per split sequence, left at 0 after each run */
+  uint64_t off_counters; /* int32 [batch]: arrivals per split sequence (fused merge), left at 0 after each run */
   uint64_t off_part_o;   /* float32 [2 * num_units, 16, 512]: normalised split partials */
   uint64_t off_part_lse; /* float32 [2 * num_units, 16]: log2-sum-exp of each partial */
 } mla_decode_plan_t;
@@ -125,9 +128,10 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
 
 /*
  * Enqueue one decode step on `stream` (kernelindex amd-mixed-mla submission
- * 690201: stage-1 split attention then the partial reduce; here the split is
- * chosen on the device and the reduce is folded into the same launch unless
- * MLA_FLAG_SEPARATE_REDUCE is set).  Pointers as in the layout table above;
+ * 690201: stage-1 split attention then the partial reduce).  The split is
+ * chosen on the device from kv_indptr; sequences split over several
+ * workgroups are merged by a second launch (or, with MLA_FLAG_FUSED_MERGE, by
+ * the last arriving workgroup).  Pointers as in the layout table above;
  * sm_scale is a host float (1/sqrt(576) in the pages).  Sequences with no KV
  * rows produce zeros.
  */

@@ -22,7 +22,7 @@ __all__ = [
     "MLA_ERR_HIP",
     "MLA_DTYPE_BF16",
     "MLA_DTYPE_FP8_E4M3FN",
-    "MLA_FLAG_SEPARATE_REDUCE",
+    "MLA_FLAG_FUSED_MERGE",
     "MlaDecodeParams",
     "MlaDecodePlan",
     "library_path",
@@ -45,7 +45,7 @@ MLA_ERR_WORKSPACE = 3
 MLA_ERR_HIP = 4
 MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP8_E4M3FN = 1
-MLA_FLAG_SEPARATE_REDUCE = 1
+MLA_FLAG_FUSED_MERGE = 1
 
 _DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3FN}
 

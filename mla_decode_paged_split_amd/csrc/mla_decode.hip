@@ -16,7 +16,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kDefaultMinChunk = 256;
-constexpr uint32_t kKnownFlags = MLA_FLAG_SEPARATE_REDUCE;
+constexpr uint32_t kKnownFlags = MLA_FLAG_FUSED_MERGE;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -177,7 +177,7 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
   a.batch = p.batch;
   a.units = p.num_units;
   a.min_chunk = p.min_chunk;
-  a.fused = (p.flags & MLA_FLAG_SEPARATE_REDUCE) ? 0 : 1;
+  a.fused = (p.flags & MLA_FLAG_FUSED_MERGE) ? 1 : 0;
 
   hipError_t err;
   if (p.q_dtype == MLA_DTYPE_BF16 && p.kv_dtype == MLA_DTYPE_BF16)
@@ -188,7 +188,7 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
     err = launch_attention<mla::Dt::FP8, mla::Dt::FP8>(a, stream);
   if (err != hipSuccess) return MLA_ERR_HIP;
   if (!a.fused) {
-    hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(p.batch), dim3(mla::kThreads), 0, stream, a);
+    hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(p.batch, mla::kHeads), dim3(64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   }
   return MLA_OK;
@@ -213,8 +213,8 @@ mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const i
   if (batch < 1 || part_indptr == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
   if (part_o == nullptr || part_lse == nullptr) return MLA_ERR_INVALID_ARG;
   if (batch > (1 << 30)) return MLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mla::mla_reduce_external_kernel, dim3(batch), dim3(mla::kThreads), 0, stream, part_o, part_lse,
-                     part_indptr, static_cast<uint16_t*>(out));
+  hipLaunchKernelGGL(mla::mla_reduce_external_kernel, dim3(batch, mla::kHeads), dim3(64), 0, stream, part_o,
+                     part_lse, part_indptr, static_cast<uint16_t*>(out));
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

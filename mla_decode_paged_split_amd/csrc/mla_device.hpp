@@ -13,7 +13,7 @@
 // [kC, (k+1)C).  A sequence that lies inside one share is finished by that
 // workgroup; one that crosses shares is split, each piece writes a
 // normalised float32 partial plus its log2-sum-exp, and the pieces are merged
-// (by a separate merge launch, or by the last arriving workgroup).  This
+// by a separate merge launch (or, optionally, by the last arriving workgroup).  This
 // plays the role of the pages' metadata partitioner and persistent work list
 // (submission 598454, get_mla_metadata_v1), but is recomputed from kv_indptr
 // inside every launch, so nothing has to be rebuilt when lengths change.
@@ -90,18 +90,11 @@ struct KvLayout<Dt::BF16> {
   static constexpr int kDepth = 2;
 };
 
-struct MergeSmem {
-  float w[64][kHeads];  // weights of the current chunk of pieces
-  float red[kWaves][kHeads];
-  float M[kHeads];
-  float inv[kHeads];
-};
 
 template <Dt KV>
 struct alignas(16) Smem {
   union {
     uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];  // V part of the current / next tile
-    MergeSmem merge;
   };
   u32x2_t p[2][kWaves][64];   // bf16 weights: wave, lane -> 4 rows of one head
   float mx[2][kWaves][kHeads];  // per-wave tile max of each head
@@ -217,81 +210,75 @@ __device__ __forceinline__ int piece_count(int st, int en, int chunk) {
 // ------------------------------------------------------------------- merge
 
 
-// Merge S partials of one query row into bf16 out_row[16][512]:
-//   out[h,:] = sum_i 2^(lse_i[h] - M[h]) o_i[h,:] / sum_i 2^(lse_i[h] - M[h]),
-// M[h] = max_i lse_i[h].  lse values are multiplied by lse_mul to bring them
-// to the log2 domain.  All 256 threads take part and every load of a pass is
-// independent of the others, so the pass costs a few memory round trips
-// rather than one per piece and head.  Thread t owns the float4 columns
-// t + 256 v (v < 8) of the flattened [16][512] row.
+// One wave merges the S partials of one head:
+//   out[h,:] = sum_i 2^(lse_i - M) o_i[h,:] / sum_i 2^(lse_i - M),  M = max_i lse_i,
+// lse multiplied by lse_mul to reach the log2 domain.  Lane i < 64 of a chunk
+// owns piece i's lse (max and weights by wavefront shuffles); lane l owns the
+// 8 output columns 8l..8l+7 and walks the pieces with the weights broadcast
+// by lane shuffles.  The first batch of partial loads is issued before the
+// lse arithmetic so a merge of a few pieces costs about one memory round trip.
 template <class SlotFn>
-__device__ void merge_pieces(const float* __restrict__ part_o, const float* __restrict__ part_lse, int S,
-                             SlotFn slot_of, float lse_mul, uint16_t* __restrict__ out_row, MergeSmem& ms) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int h = tid & 15;
-  const int r = tid >> 4;  // 0..15
-
-  // pass 1: per-head max over all pieces (wavefront shuffles, then across waves)
+__device__ void merge_head_wave(const float* __restrict__ part_o, const float* __restrict__ part_lse, int S,
+                                SlotFn slot_of, float lse_mul, int h, uint16_t* __restrict__ out_head) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kBatch = 8;
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY;
-  for (int i = r; i < S; i += 16) M = fmaxf(M, part_lse[slot_of(i) * kHeads + h] * lse_mul);
-  M = fmaxf(M, __shfl_xor(M, 16));
-  M = fmaxf(M, __shfl_xor(M, 32));
-  if (lane < 16) ms.red[w][h] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(ms.red[0][h], ms.red[1][h]), fmaxf(ms.red[2][h], ms.red[3][h]));
-  if (tid < kHeads) ms.M[tid] = M;
-
-  f32x4_t acc[8];
-#pragma unroll
-  for (int v = 0; v < 8; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float wpart = 0.f;
+  float wsum = 0.f;
   for (int i0 = 0; i0 < S; i0 += 64) {
     const int n = min(64, S - i0);
-    __syncthreads();  // the previous chunk's weights are no longer read
+    f32x4_t a[kBatch], b[kBatch];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = r + 16 * k;
-      if (i < n) {
-        const float v = part_lse[slot_of(i0 + i) * kHeads + h] * lse_mul;
-        const float wt = (v == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(v - M);
-        ms.w[i][h] = wt;
-        wpart += wt;
+    for (int u = 0; u < kBatch; ++u)
+      if (u < n) {
+        const f32x4_t* src =
+            reinterpret_cast<const f32x4_t*>(part_o + ((size_t)slot_of(i0 + u) * kHeads + h) * kVDim + lane * 8);
+        a[u] = src[0];
+        b[u] = src[1];
       }
+    const float v = (lane < n) ? part_lse[slot_of(i0 + lane) * kHeads + h] * lse_mul : -INFINITY;
+    const float m_new = fmaxf(M, wave_max(v));
+    if (m_new != M) {  // rescale what earlier chunks accumulated (uniform across the wave)
+      const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m_new);
+      acc0 *= r;
+      acc1 *= r;
+      wsum *= r;
+      M = m_new;
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int i = 0; i < n; ++i) {
-      const f32x4_t* base = reinterpret_cast<const f32x4_t*>(part_o + (size_t)slot_of(i0 + i) * kHeads * kVDim);
+    const float wt = (v == -INFINITY) ? 0.f : fast_exp2(v - M);
+    wsum += wave_sum(wt);
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int f = tid + 256 * v;
-        acc[v] += ms.w[i][f >> 7] * base[f];
+    for (int u = 0; u < kBatch; ++u)
+      if (u < n) {
+        const float wj = __shfl(wt, u);
+        acc0 += wj * a[u];
+        acc1 += wj * b[u];
       }
+    for (int j0 = kBatch; j0 < n; j0 += kBatch) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (j0 + u < n) {
+          const f32x4_t* src = reinterpret_cast<const f32x4_t*>(
+              part_o + ((size_t)slot_of(i0 + j0 + u) * kHeads + h) * kVDim + lane * 8);
+          a[u] = src[0];
+          b[u] = src[1];
+        }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (j0 + u < n) {
+          const float wj = __shfl(wt, j0 + u);
+          acc0 += wj * a[u];
+          acc1 += wj * b[u];
+        }
     }
   }
-  // per-head weight sums: 16 threads share a head (lanes l, l^16, l^32, l^48 of each wave)
-  wpart += __shfl_xor(wpart, 16);
-  wpart += __shfl_xor(wpart, 32);
-  __syncthreads();
-  if (lane < 16) ms.red[w][h] = wpart;
-  __syncthreads();
-  if (tid < kHeads) {
-    const float wsum = ms.red[0][tid] + ms.red[1][tid] + ms.red[2][tid] + ms.red[3][tid];
-    ms.inv[tid] = wsum > 0.f ? 1.0f / wsum : 0.f;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const int f = tid + 256 * v;
-    const float inv = ms.inv[f >> 7];
-    u32x2_t pk;
-    pk[0] = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
-    pk[1] = pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv);
-    *reinterpret_cast<u32x2_t*>(out_row + f * 4) = pk;
-  }
-  __syncthreads();
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  u32x4_t pk;
+  pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+  pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+  pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+  pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
+  *reinterpret_cast<u32x4_t*>(out_head + lane * 8) = pk;
 }
 
 // ------------------------------------------------------------- zero output
@@ -632,8 +619,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       if (sm.arrive == S - 1) {
         __threadfence();
         const int chunk = geo.chunk;
-        merge_pieces(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f,
-                     a.out + (size_t)t * kHeads * kVDim, sm.merge);
+        const int w = threadIdx.x >> 6;
+        for (int hh = 0; hh < kHeads / kWaves; ++hh) {
+          const int h = w * (kHeads / kWaves) + hh;
+          merge_head_wave(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f, h,
+                          a.out + ((size_t)t * kHeads + h) * kVDim);
+        }
         if (threadIdx.x == 0) atomicExch(&a.counters[b], 0);
       }
       __syncthreads();
@@ -641,10 +632,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   }
 }
 
-// Separate merge launch: one workgroup per sequence; sequences that were not
-// split were finished by the attention kernel and are skipped.
-__global__ __launch_bounds__(kThreads) void mla_merge_split_kernel(Args a) {
+// Separate merge launch: one wave per (sequence, head); sequences that were
+// not split were finished by the attention kernel and are skipped.
+__global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int b = blockIdx.x;
+  const int h = blockIdx.y;
   const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk);
   const int st = a.kv_indptr[b] - geo.base;
   const int en = a.kv_indptr[b + 1] - geo.base;
@@ -652,27 +644,20 @@ __global__ __launch_bounds__(kThreads) void mla_merge_split_kernel(Args a) {
   const int S = piece_count(st, en, geo.chunk);
   if (S <= 1) return;
   const int chunk = geo.chunk;
-  __shared__ MergeSmem ms;
-  merge_pieces(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f,
-               a.out + (size_t)a.qo_indptr[b] * kHeads * kVDim, ms);
+  merge_head_wave(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f, h,
+                  a.out + ((size_t)a.qo_indptr[b] * kHeads + h) * kVDim);
 }
 
-// Merge of caller-provided partials (natural-log lse), one workgroup per sequence.
-__global__ __launch_bounds__(kThreads) void mla_reduce_external_kernel(const float* part_o, const float* part_lse,
-                                                                       const int32_t* part_indptr, uint16_t* out) {
+// Merge of caller-provided partials (natural-log lse), one wave per (sequence, head).
+__global__ __launch_bounds__(64) void mla_reduce_external_kernel(const float* part_o, const float* part_lse,
+                                                                 const int32_t* part_indptr, uint16_t* out) {
   const int b = blockIdx.x;
+  const int h = blockIdx.y;
   const int p0 = part_indptr[b];
   const int S = part_indptr[b + 1] - p0;
-  uint16_t* out_row = out + (size_t)b * kHeads * kVDim;
-  if (S <= 0) {
-    // no parts: zeros, written cooperatively
-    u32x4_t z = {0u, 0u, 0u, 0u};
-    u32x4_t* p = reinterpret_cast<u32x4_t*>(out_row);
-    for (int i = threadIdx.x; i < kHeads * kVDim * 2 / 16; i += kThreads) p[i] = z;
-    return;
-  }
-  __shared__ MergeSmem ms;
-  merge_pieces(part_o, part_lse, S, [=](int i) { return p0 + i; }, kLog2e, out_row, ms);
+  // S <= 0 leaves all weights zero and writes zeros
+  merge_head_wave(part_o, part_lse, S < 0 ? 0 : S, [=](int i) { return p0 + i; }, kLog2e, h,
+                  out + ((size_t)b * kHeads + h) * kVDim);
 }
 
 __global__ void mla_fill_i32_kernel(int32_t* p, int n, int32_t v) {
