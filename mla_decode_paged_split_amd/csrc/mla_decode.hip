@@ -72,7 +72,10 @@ Layout layout_for(int32_t batch, int32_t units) {
 
 template <mla::Dt QT, mla::Dt KT>
 hipError_t launch_attention(const mla::Args& a, hipStream_t stream) {
-  hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT>), dim3(a.units), dim3(mla::kThreads), 0, stream, a);
+  if (a.batch <= mla::kSeqTable)
+    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, false>), dim3(a.units), dim3(mla::kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, true>), dim3(a.units), dim3(mla::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -54,6 +54,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTileRows = 64;             // KV rows per workgroup tile: 16 per wave
 constexpr int kColsPerWave = kVDim / kWaves;  // 128 output columns per wave
 constexpr int kSplitAlign = 32;           // share sizes are multiples of this
+constexpr int kScanPerThread = 4;         // sequences each thread reads in the first round trip
+constexpr int kSeqTable = kScanPerThread * kThreads;  // sequences whose indptr values are kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;     // log2 growth of the running max tolerated before rescaling
 
@@ -99,6 +101,7 @@ struct alignas(16) Smem {
   u32x2_t p[2][kWaves][64];   // bf16 weights: wave, lane -> 4 rows of one head
   float mx[2][kWaves][kHeads];  // per-wave tile max of each head
   float lsum[kWaves][kHeads];
+  int seq[kSeqTable][3];  // kv_indptr[b], kv_indptr[b+1], qo_indptr[b] of the first kSeqTable sequences
   int bmin;
   int bmax;
   int arrive;
@@ -291,12 +294,60 @@ __device__ __forceinline__ void zero_row_by_thread(uint16_t* out_row) {
 
 // --------------------------------------------------------------- one piece
 
+// The register ring of one piece: the rows of D tiles in flight (tile t in
+// slot t % D) and the row indices of the next D tiles.  Lane (c16, g) of wave
+// w owns row 16w + c16 of every 64-row tile and 16-byte chunks 4j + g of it.
+template <Dt KT>
+struct Ring {
+  static constexpr int D = KvLayout<KT>::kDepth;
+  u32x4_t dat[D][KvLayout<KT>::kChunks];
+  int first[D];  // rows of tiles 0..D-1
+  int next[D];   // rows of tiles D..2D-1, then of each slot's next refill
+};
+
+// Fetch the ring's starting indices for a piece beginning at index position
+// ip0.  Positions at or past ip_end read the piece's first index instead
+// (always a valid position).
+template <Dt KT>
+__device__ __forceinline__ void issue_ring_indices(const int32_t* __restrict__ kv_indices, int ip0, int ip_end,
+                                                   Ring<KT>& r) {
+  constexpr int D = Ring<KT>::D;
+  const int my_row = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15);
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    const int p = ip0 + k * kTileRows + my_row;
+    r.first[k] = kv_indices[p < ip_end ? p : ip0];
+  }
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    const int p = ip0 + (k + D) * kTileRows + my_row;
+    r.next[k] = kv_indices[p < ip_end ? p : ip0];
+  }
+}
+
+// Start the loads of the ring's first D tiles (in the steady state's slot
+// order, kept by scheduling barriers so the loop's wait counts stay exact).
+template <Dt KT>
+__device__ __forceinline__ void issue_ring_rows(const void* kv, Ring<KT>& r) {
+  using L = KvLayout<KT>;
+  constexpr int D = Ring<KT>::D;
+  const int g = (threadIdx.x & 63) >> 4;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(kv) + (size_t)r.first[k] * L::kRowBytes + g * 16;
+#pragma unroll
+    for (int j = 0; j < L::kChunks; ++j) r.dat[k][j] = *reinterpret_cast<const u32x4_t*>(row + j * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Attention of one query row over the index positions [ip0, ip1) (one piece
 // of one sequence).  All 256 threads take part; the workgroup writes either
 // the final bf16 row (complete) or the float32 partial in `slot`.
 template <Dt QT, Dt KT>
 __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip1, bool complete, int slot,
-                             float c_score, float out_mul) {
+                             float c_score, float out_mul, Ring<KT>& ring) {
   using L = KvLayout<KT>;
   constexpr int D = L::kDepth;
   const int lane = threadIdx.x & 63;
@@ -326,9 +377,9 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
   const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
 
-  // register ring: tile t lives in slot t % D
-  u32x4_t dat[D][L::kChunks];
-  int idxn[D];
+  // the ring arrives primed: tiles 0..D-1 in flight, indices of D..2D-1 loaded
+  auto& dat = ring.dat;
+  auto& idxn = ring.next;
   auto row_index = [&](int tt) {
     const int pos = ip0 + tt * kTileRows + my_row;
     return a.kv_indices[pos < ip1 ? pos : ip0];
@@ -338,20 +389,6 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
 #pragma unroll
     for (int j = 0; j < L::kChunks; ++j) dst[j] = *reinterpret_cast<const u32x4_t*>(row + j * 64);
   };
-  // Prologue in the steady state's load order (tile k's rows, then the index
-  // for tile k + D), kept by scheduling barriers: the loop's wait counts are
-  // computed over both the prologue and the loop back edge.
-  int idx0[D];
-#pragma unroll
-  for (int k = 0; k < D; ++k) idx0[k] = row_index(k);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int k = 0; k < D; ++k) {
-    load_tile(dat[k], idx0[k]);
-    __builtin_amdgcn_sched_barrier(0);
-    idxn[k] = row_index(k + D);
-    __builtin_amdgcn_sched_barrier(0);
-  }
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -562,9 +599,22 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
 
 // ------------------------------------------------------------------ kernels
 
-template <Dt QT, Dt KT>
+template <Dt QT, Dt KT, bool kBigBatch>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   __shared__ Smem<KT> sm;
+  // First round trip: the split geometry and the indptr values of up to
+  // kScanPerThread sequences per thread (everything the start needs, so no
+  // later load has to wait behind the ring's loads: waits count in order).
+  int sv[kScanPerThread][3];
+#pragma unroll
+  for (int i = 0; i < kScanPerThread; ++i) {
+    const int j = threadIdx.x + i * kThreads;
+    if (j < a.batch) {
+      sv[i][0] = a.kv_indptr[j];
+      sv[i][1] = a.kv_indptr[j + 1];
+      sv[i][2] = a.qo_indptr[j];
+    }
+  }
   const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk);
   const int k = blockIdx.x;
   if (k >= geo.n_wg) return;
@@ -576,14 +626,21 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   const float c_score = a.sm_scale * qs * ks * kLog2e;
   const float out_mul = ks;
 
+  // The first piece always starts at the share start (the sequence holding
+  // row lo begins at or before it), so its ring can be started now, clamped
+  // to the share, while the scan below finds the sequences.
+  Ring<KT> ring;
+  issue_ring_indices(a.kv_indices, geo.base + lo, geo.base + hi, ring);
+  issue_ring_rows<KT>(a.kv, ring);
+
   if (threadIdx.x == 0) {
     sm.bmin = 0x7fffffff;
     sm.bmax = -1;
   }
-  __syncthreads();
-  for (int j = threadIdx.x; j < a.batch; j += kThreads) {
-    const int st = a.kv_indptr[j] - geo.base;
-    const int en = a.kv_indptr[j + 1] - geo.base;
+  __syncthreads();  // bmin / bmax initialised
+  auto scan_one = [&](int j, int ipb, int ipe, int qo) {
+    const int st = ipb - geo.base;
+    const int en = ipe - geo.base;
     if (en > st) {
       if (st < hi && en > lo) {
         atomicMin(&sm.bmin, j);
@@ -593,23 +650,53 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       // an empty sequence belongs to the share holding its position
       int owner = st / geo.chunk;
       if (owner > geo.n_wg - 1) owner = geo.n_wg - 1;
-      if (owner == k) zero_row_by_thread(a.out + (size_t)a.qo_indptr[j] * kHeads * kVDim);
+      if (owner == k) zero_row_by_thread(a.out + (size_t)qo * kHeads * kVDim);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kScanPerThread; ++i) {
+    const int j = threadIdx.x + i * kThreads;
+    if (j < a.batch) {
+      if constexpr (!kBigBatch) {
+        sm.seq[j][0] = sv[i][0];
+        sm.seq[j][1] = sv[i][1];
+        sm.seq[j][2] = sv[i][2];
+      }
+      scan_one(j, sv[i][0], sv[i][1], sv[i][2]);
     }
   }
+  for (int j = threadIdx.x + kSeqTable; j < a.batch; j += kThreads)
+    scan_one(j, a.kv_indptr[j], a.kv_indptr[j + 1], a.qo_indptr[j]);
   __syncthreads();
   const int bmin = sm.bmin;
   const int bmax = sm.bmax;
 
   for (int b = bmin; b <= bmax; ++b) {
-    const int st = a.kv_indptr[b] - geo.base;
-    const int en = a.kv_indptr[b + 1] - geo.base;
+    // From the LDS table (batches up to kSeqTable), else from memory.  Two
+    // instantiations rather than a runtime select: a select between the two
+    // addresses becomes a generic load, whose wait would drain the ring.
+    int ipb, ipe, t;
+    if constexpr (!kBigBatch) {
+      ipb = sm.seq[b][0];
+      ipe = sm.seq[b][1];
+      t = sm.seq[b][2];
+    } else {
+      ipb = a.kv_indptr[b];
+      ipe = a.kv_indptr[b + 1];
+      t = a.qo_indptr[b];
+    }
+    const int st = ipb - geo.base;
+    const int en = ipe - geo.base;
     if (en <= st) continue;
     const int s_lo = max(st, lo);
     const int s_hi = min(en, hi);
     const bool complete = (st >= lo) && (en <= hi);
     const int slot = complete ? -1 : (st <= lo ? 2 * k : 2 * k + 1);
-    const int t = a.qo_indptr[b];
-    attend_piece<QT, KT>(a, sm, t, s_lo + geo.base, s_hi + geo.base, complete, slot, c_score, out_mul);
+    if (b != bmin) {
+      issue_ring_indices(a.kv_indices, s_lo + geo.base, s_hi + geo.base, ring);
+      issue_ring_rows<KT>(a.kv, ring);
+    }
+    attend_piece<QT, KT>(a, sm, t, s_lo + geo.base, s_hi + geo.base, complete, slot, c_score, out_mul, ring);
     if (!complete && a.fused) {
       __threadfence();
       __syncthreads();
