@@ -1,8 +1,9 @@
 """Benchmark one MLA-decode step on one MI355X and print one JSON line.
 
-A step is one pass of the whole path over one batch: the fp8 cast of Q when
-the workload has fp8 queries (step a0), then one mla_decode_run (work split,
-split attention and the merge of split partials).  The plan is made once: it
+A step is one pass of the whole path over one batch: one mla_decode_run
+(work split, split attention and the merge of split partials).  With fp8
+queries the attention kernel casts the bf16 Q itself (step a0 fused); with
+--separate-q-cast the step is the standalone cast launch followed by the run.  The plan is made once: it
 does not depend on the sequence lengths.
 
 Inputs are seeded synthetic tensors of the workload's shapes, resident in HBM
@@ -131,6 +132,8 @@ def main() -> int:
     ap.add_argument("--num-units", type=int, default=0)
     ap.add_argument("--min-chunk", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--separate-q-cast", action="store_true",
+                    help="fp8-Q workloads: cast Q with mla_decode_quantize_q before each run instead of in the kernel")
     ap.add_argument("--probe-copy", action="store_true", help="time a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
 
@@ -174,17 +177,19 @@ def main() -> int:
     kv_indptr = case.kv_indptr.to(dev)
     kv_scale = case.kv_scale.to(dev) if case.kv_scale is not None else None
     fp8_q = spec.q_dtype == "fp8"
-    q_in = torch.empty(q_bf16.shape, dtype=torch.uint8, device=dev) if fp8_q else q_bf16
+    sep_cast = fp8_q and args.separate_q_cast
+    q_in = torch.empty(q_bf16.shape, dtype=torch.uint8, device=dev) if sep_cast else q_bf16
     q_scale = torch.ones(1, dtype=torch.float32, device=dev) if fp8_q else None
     out = torch.empty((spec.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+    flags = args.flags | (binding.MLA_FLAG_FUSED_Q_CAST if fp8_q and not sep_cast else 0)
     dec = binding.Decoder(spec.batch, spec.q_dtype, spec.kv_dtype, dev, num_units=args.num_units,
-                          min_chunk=args.min_chunk, flags=args.flags)
+                          min_chunk=args.min_chunk, flags=flags)
     sm_scale = 1.0 / 24.0
     stream = torch.cuda.current_stream()
 
     def step(i: int, ev=None):
         r = i % R
-        if fp8_q:
+        if sep_cast:
             binding.mla_decode_quantize_q(q_bf16, q_in, stream)
         if ev is not None:
             ev[0].record(stream)
@@ -218,9 +223,9 @@ def main() -> int:
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     kern_med_ms = kern_ms[len(kern_ms) // 2]
 
-    q_elt = 1 if fp8_q else 2
+    q_elt = 1 if sep_cast else 2  # the attention launch reads fp8 Q, or bf16 Q it casts itself
     alg_bytes = algorithmic_bytes(spec, total_kv, q_elt)
-    step_bytes = alg_bytes + (q_bf16.numel() * 3 if fp8_q else 0)
+    step_bytes = alg_bytes + (q_bf16.numel() * 3 if sep_cast else 0)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
     traffic = load_traffic(args.workload, 1)
@@ -255,6 +260,7 @@ def main() -> int:
             "num_units": int(dec.plan.params.num_units),
             "min_chunk": int(dec.plan.params.min_chunk),
             "fused_merge": bool(args.flags & 1),
+            "q_cast": ("separate launch" if sep_cast else "in the attention kernel") if fp8_q else None,
         },
         "roofline": {
             "bound": "hbm",

@@ -15,7 +15,8 @@
  * (page size 1), so a row index is a page index.
  *
  * Layouts (all row-major, contiguous, device memory unless stated):
- *   q          [total_q, 16, 576]   bf16 or fp8 e4m3fn
+ *   q          [total_q, 16, 576]   bf16 or fp8 e4m3fn (bf16 also with fp8 q_dtype
+ *                                   when MLA_FLAG_FUSED_Q_CAST is set)
  *   kv         [pool_rows, 576]     bf16 or fp8 e4m3fn (one KV head, page size 1)
  *   qo_indptr  [batch + 1]          int32, query rows of sequence b
  *   kv_indptr  [batch + 1]          int32, index positions of sequence b
@@ -71,6 +72,10 @@ typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP8_E4M3FN = 1 } mla_dtype;
                                    slower on MI355X: the device-scope release /
                                    acquire it needs writes back and invalidates
                                    the per-XCD L2 in every split workgroup. */
+#define MLA_FLAG_FUSED_Q_CAST 2u /* with q_dtype = fp8: `q` holds bf16 values and
+                                    the attention kernel casts them to fp8
+                                    e4m3fn itself, bit-identically to
+                                    mla_decode_quantize_q (saves its launch) */
 
 /*
  * Problem description.  The fixed fields restate the model constants of

@@ -23,6 +23,7 @@ __all__ = [
     "MLA_DTYPE_BF16",
     "MLA_DTYPE_FP8_E4M3FN",
     "MLA_FLAG_FUSED_MERGE",
+    "MLA_FLAG_FUSED_Q_CAST",
     "MlaDecodeParams",
     "MlaDecodePlan",
     "library_path",
@@ -46,6 +47,7 @@ MLA_ERR_HIP = 4
 MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP8_E4M3FN = 1
 MLA_FLAG_FUSED_MERGE = 1
+MLA_FLAG_FUSED_Q_CAST = 2
 
 _DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3FN}
 

@@ -16,7 +16,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kDefaultMinChunk = 256;
-constexpr uint32_t kKnownFlags = MLA_FLAG_FUSED_MERGE;
+constexpr uint32_t kKnownFlags = MLA_FLAG_FUSED_MERGE | MLA_FLAG_FUSED_Q_CAST;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -38,6 +38,7 @@ mla_status validate_params(const mla_decode_params* p) {
     return MLA_ERR_UNSUPPORTED;
   if (p->total_q != p->batch) return MLA_ERR_UNSUPPORTED;  // one decode token per sequence
   if (p->q_dtype == MLA_DTYPE_FP8_E4M3FN && p->kv_dtype == MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if ((p->flags & MLA_FLAG_FUSED_Q_CAST) && p->q_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_INVALID_ARG;
   if (p->num_units > (1 << 20)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
@@ -181,6 +182,7 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
   a.units = p.num_units;
   a.min_chunk = p.min_chunk;
   a.fused = (p.flags & MLA_FLAG_FUSED_MERGE) ? 1 : 0;
+  a.q_cast = (p.flags & MLA_FLAG_FUSED_Q_CAST) ? 1 : 0;
 
   hipError_t err;
   if (p.q_dtype == MLA_DTYPE_BF16 && p.kv_dtype == MLA_DTYPE_BF16)

@@ -124,6 +124,7 @@ struct Args {
   int32_t units;
   int32_t min_chunk;
   int32_t fused;
+  int32_t q_cast;  // fp8 Q given as bf16: cast in the kernel (same rounding as mla_quantize_q_kernel)
 };
 
 // ------------------------------------------------------------------ helpers
@@ -173,6 +174,74 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// bf16 -> fp8 e4m3fn, round to nearest even, non-saturating (magnitudes above
+// 464, infinities and NaN give the NaN code with the input's sign).  Integer
+// arithmetic on the bit fields, so the result does not depend on any
+// hardware conversion mode.
+__device__ __forceinline__ uint32_t bf16_to_e4m3fn(uint32_t x) {
+  const uint32_t sign = (x >> 8) & 0x80u;
+  const int e = (int)((x >> 7) & 0xFFu);
+  const uint32_t m = x & 0x7Fu;
+  if (e == 0xFF) return sign | 0x7Fu;
+  int E = e - 127 + 7;  // e4m3 biased exponent
+  if (E >= 1) {
+    uint32_t m3 = m >> 4;
+    const uint32_t rem = m & 0xFu;
+    if (rem > 8u || (rem == 8u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) {
+      m3 = 0;
+      ++E;
+    }
+    if (E > 15 || (E == 15 && m3 == 7u)) return sign | 0x7Fu;
+    return sign | ((uint32_t)E << 3) | m3;
+  }
+  // below 2^-6: units of 2^-9 (the e4m3 subnormal step)
+  const int shift = 125 - e;  // significand (with hidden bit) is 8 bits wide
+  if (e == 0 || shift > 9) return sign;  // bf16 subnormals and anything below 2^-10 round to zero
+  const uint32_t sig = 0x80u | m;
+  uint32_t n = sig >> shift;
+  const uint32_t rem = sig & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (n & 1u))) ++n;
+  return sign | n;  // n == 8 is the smallest normal, encoded the same way
+}
+
+// Eight bf16 Q values (four dwords) -> eight e4m3fn bytes with the same
+// rounding as bf16_to_e4m3fn.  The hardware conversion (low-word form, scale
+// 1) agrees with it on every non-NaN input; it gives a positive NaN the
+// negative NaN code, so a lane whose values hold a positive NaN redoes the
+// cast bit by bit.  Each pair is converted into the low word of a fresh
+// register and the pairs are joined with shifts.  The pair goes through a
+// named scalar: hipcc lowers __builtin_bit_cast of an ext-vector subscript
+// to element 0 whatever the index.
+__device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w, uint32_t& posnan) {
+  typedef short short2v __attribute__((ext_vector_type(2)));
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t pair = w[i];
+    const short2v o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(short2v{0, 0}, __builtin_bit_cast(bf16x2_t, pair),
+                                                                1.0f, false);
+    p[i] = __builtin_bit_cast(uint32_t, o) & 0xFFFFu;
+  }
+  const uint32_t r[2] = {p[0] | (p[1] << 16), p[2] | (p[3] << 16)};
+  // a half h is a NaN iff (h & 0x7fff) + 0x7f carries into bit 15; positive iff its sign bit is clear
+#pragma unroll
+  for (int i = 0; i < 4; ++i) posnan |= ((w[i] & 0x7fff7fffu) + 0x007f007fu) & ~w[i] & 0x80008000u;
+  return (uint64_t)r[0] | ((uint64_t)r[1] << 32);
+}
+
+__device__ __forceinline__ uint64_t bf16x8_to_e4m3fn_exact(u32x4_t w) {
+  uint64_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t lo = bf16_to_e4m3fn(w[i] & 0xFFFFu);
+    const uint64_t hi = bf16_to_e4m3fn(w[i] >> 16);
+    out |= (lo | (hi << 8)) << (16 * i);
+  }
+  return out;
 }
 
 // ---------------------------------------------------------------- partition
@@ -367,9 +436,35 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
     if constexpr (QT == Dt::BF16) {
       qb[s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(a.q) +
                                                  ((size_t)t * kHeads + c16) * kQKDim + d0);
-    } else {
+    } else if (!a.q_cast) {
       q8[s] = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) +
                                                  ((size_t)t * kHeads + c16) * kQKDim + d0);
+    }
+  }
+  if constexpr (QT == Dt::FP8) {
+    if (a.q_cast) {  // fp8 Q supplied as bf16 (uniform branch)
+      u32x4_t qw[kSteps];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int d0 = ((s >> 1) * 4 + g) * 16 + (s & 1) * 8;
+        qw[s] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                 ((size_t)t * kHeads + c16) * kQKDim + d0);
+      }
+      uint32_t posnan = 0;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) q8[s] = bf16x8_to_e4m3fn(qw[s], posnan);
+      if (__builtin_amdgcn_ballot_w64(posnan != 0u) != 0ull && posnan != 0u) {
+        // rare: a positive NaN in this lane's values; reload them and cast bit by bit
+        for (int s = 0; s < kSteps; ++s) {
+          const int d0 = ((s >> 1) * 4 + g) * 16 + (s & 1) * 8;
+          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                              ((size_t)t * kHeads + c16) * kQKDim + d0);
+          const uint64_t v = bf16x8_to_e4m3fn_exact(w);
+#pragma unroll
+          for (int s2 = 0; s2 < kSteps; ++s2)
+            if (s2 == s) q8[s2] = v;
+        }
+      }
     }
   }
 
@@ -754,53 +849,18 @@ __global__ void mla_fill_i32_kernel(int32_t* p, int n, int32_t v) {
 
 // ------------------------------------------------------------ step a0: Q cast
 
-// bf16 -> fp8 e4m3fn, round to nearest even, non-saturating (magnitudes above
-// 464, infinities and NaN give the NaN code with the input's sign).  Integer
-// arithmetic on the bit fields, so the result does not depend on any
-// hardware conversion mode.
-__device__ __forceinline__ uint32_t bf16_to_e4m3fn(uint32_t x) {
-  const uint32_t sign = (x >> 8) & 0x80u;
-  const int e = (int)((x >> 7) & 0xFFu);
-  const uint32_t m = x & 0x7Fu;
-  if (e == 0xFF) return sign | 0x7Fu;
-  int E = e - 127 + 7;  // e4m3 biased exponent
-  if (E >= 1) {
-    uint32_t m3 = m >> 4;
-    const uint32_t rem = m & 0xFu;
-    if (rem > 8u || (rem == 8u && (m3 & 1u))) ++m3;
-    if (m3 == 8u) {
-      m3 = 0;
-      ++E;
-    }
-    if (E > 15 || (E == 15 && m3 == 7u)) return sign | 0x7Fu;
-    return sign | ((uint32_t)E << 3) | m3;
-  }
-  // below 2^-6: units of 2^-9 (the e4m3 subnormal step)
-  const int shift = 125 - e;  // significand (with hidden bit) is 8 bits wide
-  if (e == 0 || shift > 9) return sign;  // bf16 subnormals and anything below 2^-10 round to zero
-  const uint32_t sig = 0x80u | m;
-  uint32_t n = sig >> shift;
-  const uint32_t rem = sig & ((1u << shift) - 1u);
-  const uint32_t half = 1u << (shift - 1);
-  if (rem > half || (rem == half && (n & 1u))) ++n;
-  return sign | n;  // n == 8 is the smallest normal, encoded the same way
-}
-
+// Step a0: groups of eight through the same conversion the attention kernel
+// uses for a bf16-supplied fp8 Q (so the exhaustive test of this kernel
+// covers both); unaligned heads and tails go value by value.
 __global__ void mla_quantize_q_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n; i += stride) {
     if (i + 8 <= n && ((reinterpret_cast<uintptr_t>(src + i) & 15u) == 0) && ((reinterpret_cast<uintptr_t>(dst + i) & 7u) == 0)) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + i);
-      u32x2_t o;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t a0 = bf16_to_e4m3fn(v[2 * k] & 0xFFFFu);
-        const uint32_t a1 = bf16_to_e4m3fn(v[2 * k] >> 16);
-        const uint32_t a2 = bf16_to_e4m3fn(v[2 * k + 1] & 0xFFFFu);
-        const uint32_t a3 = bf16_to_e4m3fn(v[2 * k + 1] >> 16);
-        o[k] = a0 | (a1 << 8) | (a2 << 16) | (a3 << 24);
-      }
-      *reinterpret_cast<u32x2_t*>(dst + i) = o;
+      uint32_t posnan = 0;
+      uint64_t o = bf16x8_to_e4m3fn(v, posnan);
+      if (posnan) o = bf16x8_to_e4m3fn_exact(v);
+      *reinterpret_cast<uint64_t*>(dst + i) = o;
     } else {
       for (int64_t j = i; j < n && j < i + 8; ++j) dst[j] = (uint8_t)bf16_to_e4m3fn(src[j]);
     }

@@ -50,11 +50,16 @@ class DevCase:
     def decoder(self, **kw) -> binding.Decoder:
         return binding.Decoder(self.batch, self.q_dtype, self.kv_dtype, self.dev, **kw)
 
-    def run(self, dec: binding.Decoder | None = None, out: torch.Tensor | None = None, **kw) -> torch.Tensor:
+    def run(self, dec: binding.Decoder | None = None, out: torch.Tensor | None = None, q_cast: bool = False,
+            **kw) -> torch.Tensor:
+        """One decode step; with q_cast the fp8 Q is cast inside the attention kernel from the bf16 Q."""
+        if q_cast:
+            kw["flags"] = kw.get("flags", 0) | binding.MLA_FLAG_FUSED_Q_CAST
         dec = dec or self.decoder(**kw)
         if out is None:
             out = torch.full((self.batch, 16, 512), float("nan"), dtype=torch.bfloat16, device=self.dev)
-        dec.run(self.q, self.kv, self.qo_indptr, self.kv_indptr, self.kv_indices, self.q_scale, self.kv_scale,
+        q = self.q_bf16 if q_cast else self.q
+        dec.run(q, self.kv, self.qo_indptr, self.kv_indptr, self.kv_indices, self.q_scale, self.kv_scale,
                 oracle.SM_SCALE, out)
         return out
 

@@ -71,6 +71,7 @@ def test_workspace_size_is_host_arithmetic():
         (dict(min_chunk=33), B.MLA_ERR_INVALID_ARG),
         (dict(min_chunk=-32), B.MLA_ERR_INVALID_ARG),
         (dict(flags=8), B.MLA_ERR_INVALID_ARG),
+        (dict(q_dtype="fp8", flags=B.MLA_FLAG_FUSED_Q_CAST | 8), B.MLA_ERR_INVALID_ARG),
         (dict(q_dtype=7), B.MLA_ERR_INVALID_ARG),
         (dict(num_heads=8), B.MLA_ERR_UNSUPPORTED),
         (dict(num_kv_heads=2), B.MLA_ERR_UNSUPPORTED),
@@ -79,6 +80,8 @@ def test_workspace_size_is_host_arithmetic():
         (dict(page_size=16), B.MLA_ERR_UNSUPPORTED),
         (dict(total_q=8), B.MLA_ERR_UNSUPPORTED),
         (dict(q_dtype="fp8", kv_dtype="bf16"), B.MLA_ERR_UNSUPPORTED),
+        (dict(flags=B.MLA_FLAG_FUSED_Q_CAST), B.MLA_ERR_INVALID_ARG),  # needs fp8 q_dtype
+        (dict(flags=4), B.MLA_ERR_INVALID_ARG),
     ],
 )
 def test_plan_rejects_bad_params_before_any_hip_call(kw, code):

@@ -21,7 +21,7 @@ PAIRS = [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8")]
 LENGTHS = [1, 2, 31, 32, 33, 64, 100, 257, 513, 1000, 2053]
 # (num_units, min_chunk, flags): one share for everything, a few shares, many
 # shares, and 32-row shares (up to 65 pieces for the 2053-row sequence)
-SPLITS = [(1, 32, 0), (8, 32, 0), (8, 32, 1), (256, 32, 0), (4096, 32, 0), (4096, 32, 1)]
+SPLITS = [(1, 32, 0), (8, 32, 0), (8, 32, 1), (256, 32, 0), (4096, 32, 0), (4096, 32, 1)]  # flag 1: fused merge
 
 
 def test_device_facts(gpu):
@@ -204,3 +204,45 @@ def test_lengths_change_without_replanning(gpu):
         case = synth.make_case(synth.CaseSpec(batch=3, q_dtype="bf16", kv_dtype="fp8", lengths=lens, seed=950 + step))
         dc = DevCase(case, gpu)
         assert_parity(oracle_ref(case), to64(dc.run(dec)), f"step{step}")
+
+
+def _edge_q(case):
+    """Put fp8 rounding ties, subnormal-range values and signed zeros into Q (the full code range is covered by
+    the exhaustive cast test, which goes through the same eight-value conversion)."""
+    q = case.q_bf16.clone()
+    edge = torch.tensor([1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -11, -2.0 ** -10, 2.0 ** -7, 0.0, -0.0,
+                         0.0156, 1.5, 2.25], dtype=torch.float32).to(torch.bfloat16)
+    q.view(-1)[: edge.numel() * 97: 97] = edge  # scattered over heads and dims
+    return q
+
+
+@pytest.mark.parametrize("units", [1, 8, 256])
+def test_fused_q_cast_matches_separate_cast(gpu, units):
+    spec = synth.CaseSpec(batch=5, q_dtype="fp8", kv_dtype="fp8", lengths=[1, 70, 600, 2100, 33], permuted=True,
+                          extra_pool_rows=11, seed=1100)
+    case = synth.make_case(spec)
+    case.q_bf16 = _edge_q(case)
+    dc = DevCase(case, gpu)  # casts Q with mla_decode_quantize_q (step a0)
+    sep = dc.run(num_units=units, min_chunk=32).cpu()
+    fused = dc.run(num_units=units, min_chunk=32, q_cast=True).cpu()
+    assert torch.equal(sep.view(torch.int16), fused.view(torch.int16))
+    assert_parity(oracle_ref(case), to64(fused), f"fused cast u{units}")
+
+
+def test_fused_q_cast_positive_nan_fallback(gpu):
+    """A positive NaN in Q sends its lane through the exact conversion; the other lanes of the wave keep the
+    hardware result, so every other head and sequence matches the separately cast Q bit for bit."""
+    spec = synth.CaseSpec(batch=3, q_dtype="fp8", kv_dtype="fp8", lengths=[40, 300, 90], seed=1200)
+    case = synth.make_case(spec)
+    q = case.q_bf16.view(torch.int16).clone()
+    q[1, 5, 17] = 0x7FC1  # positive NaN: the hardware cast gives the negative NaN code, the fallback fixes it
+    q[2, 0, 3] = -0x7F7F  # bits 0x8081: a negative subnormal
+    case.q_bf16 = q.view(torch.bfloat16)
+    dc = DevCase(case, gpu)
+    q8 = dc.q.cpu().numpy()
+    assert q8[1, 5, 17] == 0x7F  # the standalone cast keeps the NaN's sign
+    sep = dc.run(num_units=4, min_chunk=32).cpu()
+    fused = dc.run(num_units=4, min_chunk=32, q_cast=True).cpu()
+    assert torch.equal(sep.view(torch.int16), fused.view(torch.int16))
+    ok = torch.isfinite(fused.float())
+    assert not bool(ok[1, 5].any()) and bool(ok[0].all()) and bool(ok[2].all())
