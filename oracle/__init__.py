@@ -10,17 +10,25 @@ Sources (the kernelindex amd-mixed-mla submission pages):
 
 * ``formats``  -- exact bf16 / e4m3fn decoding from the field definitions and
   the round-to-nearest-even cast of bf16 Q to e4m3fn (submission 689529,
-  docstring and ``custom_kernel``: Q cast straight to fp8 with unit scale).
+  docstring and ``custom_kernel``: Q cast straight to fp8 with unit scale),
+  plus the per-tensor amax-scaled cast that docstring names as skipped.
 * ``mla``      -- the decode itself (submission 689529 constants block and
   ``custom_kernel``; submission 690201 stage-1 and reduce calls), split
-  partials and their log-sum-exp merge.
+  partials and their log-sum-exp merge; pages of several rows, several
+  causal query tokens per sequence and the logit soft-cap.
 
 Pins (tests marked "not gpu" in ``tests/test_oracle.py``): exhaustive format
 checks against torch's CPU casts, float64 scaled-dot-product attention as the
 multi-query special case, a pure-Python brute force, closed forms (one row,
 q = 0, constant V, two rows, dominant row, duplicated row), split/merge
-invariance, and deliberately wrong variants that must fail.  No function here
-is "parity unpinned".
+invariance, and deliberately wrong variants that must fail.  The widened
+forms: the soft-cap against its limits (cap -> 0 gives the mean of V, a huge
+cap the plain result) and a 3:1 closed form through atanh(1/2); pages
+against a hand-worked row expansion and against the same rows laid out one
+per page; several query tokens against torch's scaled-dot-product attention
+(no mask, and the square causal mask when every row is a query); the
+amax-scaled cast against torch's float32 division and e4m3fn cast.  No
+function here is "parity unpinned".
 """
 
 from .formats import (  # noqa: F401
@@ -31,6 +39,7 @@ from .formats import (  # noqa: F401
     decode_fp8_e4m3fn,
     encode_bf16_rne,
     encode_fp8_e4m3fn,
+    quantize_q_dynamic,
 )
 from .mla import (  # noqa: F401
     NUM_HEADS,
@@ -43,4 +52,7 @@ from .mla import (  # noqa: F401
     mla_decode,
     mla_decode_bruteforce,
     mla_decode_sequence,
+    paged_rows,
+    soft_cap,
+    visible_rows,
 )

@@ -33,6 +33,7 @@ __all__ = [
     "decode_fp8_e4m3fn",
     "encode_fp8_e4m3fn",
     "encode_bf16_rne",
+    "quantize_q_dynamic",
     "BF16_TABLE",
     "FP8_TABLE",
 ]
@@ -140,6 +141,35 @@ def bf16_bits_to_fp8_bits(bits: np.ndarray) -> np.ndarray:
     if _BF16_TO_FP8 is None:
         _BF16_TO_FP8 = encode_fp8_e4m3fn(BF16_TABLE)
     return _BF16_TO_FP8[np.asarray(bits).astype(np.uint16, copy=False)]
+
+
+def quantize_q_dynamic(bits: np.ndarray) -> tuple[np.ndarray, float]:
+    """bf16 Q -> (e4m3fn codes, float32 per-tensor scale), the amax variant of the Q cast.
+
+    The pages cast Q with a unit scale and name the per-tensor amax pass as
+    the step they skipped (submission 689529 docstring).  Reading of that
+    step, in the same form as the KV scale the pages pair with fp8 KV:
+
+    * amax = the largest |q| over the finite values (bf16 is exact in float32);
+    * q_scale = amax / 448 in float32 (1 when amax is 0: nothing to scale);
+    * each finite q is divided by q_scale in float32 and cast to e4m3fn with
+      round-to-nearest-even; +-inf and NaN inputs give the NaN code with the
+      input's sign.
+
+    The dequantised value is code * q_scale.  The float32 division is the
+    precision the device kernel uses; it decides the codes, so both sides
+    take it in float32.
+    """
+    bits = np.asarray(bits).astype(np.uint16, copy=False)
+    x = decode_bf16(bits)
+    finite = np.isfinite(x)
+    amax = np.float32(np.max(np.abs(x[finite]))) if finite.any() else np.float32(0.0)
+    scale = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
+    y = np.where(finite, x, 0.0).astype(np.float32) / scale  # float32 division, correctly rounded
+    codes = encode_fp8_e4m3fn(y.astype(np.float64))
+    sign = ((bits >> 8) & 0x80).astype(np.uint8)
+    codes = np.where(finite, codes, sign | np.uint8(0x7F)).astype(np.uint8)
+    return codes, float(scale)
 
 
 def encode_bf16_rne(x: np.ndarray) -> np.ndarray:

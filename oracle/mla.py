@@ -19,6 +19,24 @@ constants and ``custom_kernel``; submission 690201, the direct stage-1 call):
   (``q_scale``, ``kv_scale``, passed next to the fp8 tensors in the submission
   690201 stage-1 call).  bf16 operands take no scale.
 
+Widened forms (arguments the pages pass to the decode and metadata calls:
+pages of 2 and 8 rows with ``kv_last_page_lens`` in submission 598454's
+a8w8 path and submission 641982's dispatch; ``q_seq_len``, ``is_causal`` and
+``logit_cap`` in submission 689529's cache builder and ``custom_kernel``):
+
+* pages of ``page_size`` rows: the pool is ``[num_pages * page_size, D]``,
+  ``kv_indices`` names pages and the last page of sequence b holds
+  ``kv_last_page_len[b]`` rows (read as clamped into ``[1, page_size]``:
+  submission 689529 passes the sequence length there with page size 1,
+  which this reading turns into "every page full");
+* several query tokens per sequence (``qo_indptr``); with ``causal`` token i
+  of a sequence with q_len tokens and L rows sees its first
+  ``L - q_len + 1 + i`` rows (the tokens are the sequence's last rows), else
+  all L rows;
+* ``logit_cap > 0`` replaces every score s by ``logit_cap * tanh(s / logit_cap)``
+  before the softmax (the pages pass 0, i.e. off, and do not print the
+  formula; this is the usual soft-cap reading).
+
 Every value is decoded exactly from its bits (``oracle.formats``), all
 arithmetic is float64 numpy, and sequences are processed one at a time.
 """
@@ -38,6 +56,9 @@ __all__ = [
     "V_DIM",
     "SM_SCALE",
     "decode_operand",
+    "soft_cap",
+    "paged_rows",
+    "visible_rows",
     "mla_decode",
     "mla_decode_sequence",
     "mla_decode_bruteforce",
@@ -66,17 +87,53 @@ def decode_operand(bits: np.ndarray, dtype: str, scale: float | None) -> np.ndar
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def mla_decode_sequence(Q: np.ndarray, K: np.ndarray, sm_scale: float, v_dim: int = V_DIM) -> np.ndarray:
+def soft_cap(S: np.ndarray, logit_cap: float) -> np.ndarray:
+    """Scores through the logit soft-cap: cap * tanh(S / cap) for cap > 0, S unchanged for cap == 0."""
+    if logit_cap == 0:
+        return S
+    if not logit_cap > 0:
+        raise ValueError("logit_cap must be >= 0")
+    return logit_cap * np.tanh(S / logit_cap)
+
+
+def paged_rows(kv_indptr, kv_indices, b: int, page_size: int = 1, kv_last_page_len=None) -> np.ndarray:
+    """Pool rows of sequence b, in order: every slot of each page, the last page cut to its length.
+
+    Page p holds pool rows ``p * page_size .. p * page_size + page_size - 1``.
+    ``kv_last_page_len`` None means every page is full.
+    """
+    p0, p1 = int(kv_indptr[b]), int(kv_indptr[b + 1])
+    if p1 <= p0:
+        return np.zeros(0, dtype=np.int64)
+    last = page_size if kv_last_page_len is None else min(max(int(kv_last_page_len[b]), 1), page_size)
+    rows = []
+    for i in range(p0, p1):
+        page = int(kv_indices[i])
+        n = page_size if i < p1 - 1 else last
+        rows.extend(page * page_size + s for s in range(n))
+    return np.asarray(rows, dtype=np.int64)
+
+
+def visible_rows(n_rows: int, q_len: int, i: int, causal: bool) -> int:
+    """How many of a sequence's n_rows rows its query token i (of q_len) sees."""
+    if not causal:
+        return n_rows
+    return max(0, min(n_rows, n_rows - q_len + 1 + i))
+
+
+def mla_decode_sequence(Q: np.ndarray, K: np.ndarray, sm_scale: float, v_dim: int = V_DIM,
+                        logit_cap: float = 0.0) -> np.ndarray:
     """One sequence: Q [H, D] and K [n, D] float64 -> O [H, v_dim] float64.
 
-    softmax over the n rows of sm_scale * Q K^T, then times the first v_dim
-    columns of the same rows.  n == 0 gives zeros (an empty sequence attends
-    to nothing; the pages never form one).
+    softmax over the n rows of the (optionally soft-capped) scores
+    sm_scale * Q K^T, then times the first v_dim columns of the same rows.
+    n == 0 gives zeros (an empty sequence attends to nothing; the pages never
+    form one).
     """
     H = Q.shape[0]
     if K.shape[0] == 0:
         return np.zeros((H, v_dim), dtype=np.float64)
-    S = sm_scale * (Q @ K.T)  # [H, n]
+    S = soft_cap(sm_scale * (Q @ K.T), logit_cap)  # [H, n]
     S = S - S.max(axis=1, keepdims=True)
     P = np.exp(S)
     P /= P.sum(axis=1, keepdims=True)
@@ -97,12 +154,17 @@ def mla_decode(
     sm_scale: float = SM_SCALE,
     v_dim: int = V_DIM,
     sequences: Sequence[int] | None = None,
+    page_size: int = 1,
+    kv_last_page_len: Sequence[int] | None = None,
+    causal: bool = False,
+    logit_cap: float = 0.0,
 ) -> np.ndarray:
     """Full paged MLA decode in float64.
 
     q_bits  [total_q, H, D] (uint16 for bf16, uint8 for fp8)
-    kv_bits [rows, D]       (uint16 for bf16, uint8 for fp8); the page-size-1
-                            pool with its single KV head squeezed out.
+    kv_bits [pool_rows, D]  (uint16 for bf16, uint8 for fp8); the pool of
+                            ``pool_rows / page_size`` pages with its single KV
+                            head squeezed out.
     Returns O [total_q, H, v_dim] float64.  With ``sequences`` given, only the
     query rows of those sequences are computed (the rest stay zero), which lets
     a test sample a large batch.
@@ -117,11 +179,14 @@ def mla_decode(
     out = np.zeros((total_q, H, v_dim), dtype=np.float64)
     seqs = range(B) if sequences is None else sequences
     for b in seqs:
-        rows = kv_indices[kv_indptr[b] : kv_indptr[b + 1]]
+        rows = paged_rows(kv_indptr, kv_indices, b, page_size, kv_last_page_len)
         K = decode_operand(kv_bits[rows], kv_dtype, kv_scale)
-        for t in range(qo_indptr[b], qo_indptr[b + 1]):
+        q_len = int(qo_indptr[b + 1] - qo_indptr[b])
+        for i in range(q_len):
+            t = int(qo_indptr[b]) + i
+            n = visible_rows(len(rows), q_len, i, causal)
             Q = decode_operand(q_bits[t], q_dtype, q_scale)
-            out[t] = mla_decode_sequence(Q, K, sm_scale, v_dim)
+            out[t] = mla_decode_sequence(Q, K[:n], sm_scale, v_dim, logit_cap)
     return out
 
 

@@ -395,3 +395,214 @@ def test_generator_is_seeded_and_shaped():
     # per-tensor scale maps the largest magnitude onto the fp8 maximum
     assert a.kv.view(torch.uint8).numpy().view(np.uint8).max() in (0x7E, 0xFE) or \
         np.abs(formats.decode_fp8_e4m3fn(a.kv.view(torch.uint8).numpy())).max() == 448.0
+
+
+# ------------------------------------------------------------ logit soft-cap
+
+
+def test_soft_cap_zero_is_off_and_large_cap_is_plain():
+    rng = np.random.default_rng(51)
+    Q, K = _seq(rng, 200, 2.0)
+    plain = mla.mla_decode_sequence(Q, K, mla.SM_SCALE)
+    assert np.array_equal(mla.mla_decode_sequence(Q, K, mla.SM_SCALE, logit_cap=0.0), plain)
+    # cap * tanh(s / cap) = s - s^3 / (3 cap^2) + ...: scores of size ~5 move by ~1e-11 at cap 1e6
+    assert np.max(np.abs(mla.mla_decode_sequence(Q, K, mla.SM_SCALE, logit_cap=1e6) - plain)) <= 1e-9
+
+
+def test_soft_cap_tiny_cap_flattens_to_mean_of_v():
+    rng = np.random.default_rng(52)
+    Q, K = _seq(rng, 33, 5.0)
+    O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE, logit_cap=1e-9)  # every capped score is within 1e-9 of 0
+    assert np.max(np.abs(O - K[:, :512].mean(axis=0))) <= 1e-8
+
+
+def test_soft_cap_three_to_one_closed_form():
+    """Two rows whose scaled scores are cap*atanh(1/2) and 0: capped they are cap/2 and 0,
+    and with cap = 2 ln 3 the softmax weights are exactly 3/4 and 1/4 for every head."""
+    rng = np.random.default_rng(53)
+    cap = 2.0 * math.log(3.0)
+    Q = rng.standard_normal((16, 576))
+    target = cap * math.atanh(0.5) / mla.SM_SCALE  # raw dot product wanted for row 0, all heads
+    k0 = Q.T @ np.linalg.solve(Q @ Q.T, np.full(16, target))  # least-norm solution of Q k0 = target
+    k1 = rng.standard_normal(576)
+    k1 -= Q.T @ np.linalg.solve(Q @ Q.T, Q @ k1)  # orthogonal to every head's query: score 0
+    K = np.stack([k0, k1])
+    assert np.max(np.abs(Q @ k1)) <= 1e-9 and np.max(np.abs(Q @ k0 - target)) <= 1e-9
+    O = mla.mla_decode_sequence(Q, K, mla.SM_SCALE, logit_cap=cap)
+    assert np.max(np.abs(O - (0.75 * k0[:512] + 0.25 * k1[:512]))) <= 1e-9 * np.max(np.abs(K))
+    # a cap applied before sm_scale, or tanh without the 1/cap inside, misses this value
+    wrong = mla.soft_cap(Q @ K.T, cap) * mla.SM_SCALE
+    assert not np.allclose(np.exp(wrong[:, 0] - wrong[:, 1]), 3.0, rtol=1e-3)
+    assert not np.allclose(cap * np.tanh(mla.SM_SCALE * (Q @ k0)), cap / 2, rtol=1e-3)
+
+
+def test_soft_cap_rejects_negative():
+    with pytest.raises(ValueError):
+        mla.soft_cap(np.zeros(3), -1.0)
+
+
+# ------------------------------------------------------------------ pages
+
+
+def test_paged_rows_worked_example():
+    kv_indptr = [0, 2, 3, 3]
+    kv_indices = [5, 2, 7]
+    # page p of 4 rows holds pool rows 4p..4p+3; last pages hold 3, 4 and (empty sequence) - rows
+    assert oracle.paged_rows(kv_indptr, kv_indices, 0, 4, [3, 4, 1]).tolist() == [20, 21, 22, 23, 8, 9, 10]
+    assert oracle.paged_rows(kv_indptr, kv_indices, 1, 4, [3, 4, 1]).tolist() == [28, 29, 30, 31]
+    assert oracle.paged_rows(kv_indptr, kv_indices, 2, 4, [3, 4, 1]).tolist() == []
+    # lengths outside [1, page_size] clamp: 9 -> 4 (full), 0 -> 1
+    assert oracle.paged_rows(kv_indptr, kv_indices, 0, 4, [9, 0, 1]).tolist() == [20, 21, 22, 23, 8, 9, 10, 11]
+    assert oracle.paged_rows(kv_indptr, kv_indices, 1, 4, [9, 0, 1]).tolist() == [28]
+    # no lengths: every page full; page size 1: the indices themselves
+    assert oracle.paged_rows(kv_indptr, kv_indices, 0, 2).tolist() == [10, 11, 4, 5]
+    assert oracle.paged_rows(kv_indptr, kv_indices, 0, 1).tolist() == [5, 2]
+
+
+@pytest.mark.parametrize("ps", [2, 8, 16])
+def test_paged_pool_equals_row_pool(ps):
+    """The same logical rows laid into pages of ps rows (pages shuffled, the tail of each
+    last page filled with junk) give the page-size-1 result."""
+    rng = np.random.default_rng(60 + ps)
+    lens = [1, ps, ps + 1, 3 * ps - 1, 100]
+    B = len(lens)
+    q_bits, kv_bits, qo, kvp, idx, _ = _rand_case(rng, B, lens)
+    ref = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16")
+    pages_per = [(n + ps - 1) // ps for n in lens]
+    n_pages = sum(pages_per) + 3
+    order = rng.permutation(n_pages)
+    pool = rng.integers(-30000, 30000, size=(n_pages * ps, 576)).astype(np.int16)  # junk everywhere
+    kv_indices, last, nxt = [], [], 0
+    for b, n in enumerate(lens):
+        for pg in range(pages_per[b]):
+            page = int(order[nxt])
+            nxt += 1
+            kv_indices.append(page)
+            for s in range(ps):
+                r = pg * ps + s
+                if r < n:
+                    pool[page * ps + s] = kv_bits[idx[kvp[b] + r]]
+        last.append(n - (pages_per[b] - 1) * ps)
+    page_indptr = np.concatenate([[0], np.cumsum(pages_per)])
+    got = oracle.mla_decode(q_bits, pool, qo, page_indptr, kv_indices, q_dtype="bf16", kv_dtype="bf16",
+                            page_size=ps, kv_last_page_len=last)
+    assert np.array_equal(got, ref)
+
+
+def test_page_size_one_with_sequence_length_as_last_len():
+    # one page passes the sequence length as the last-page length with page size 1: every page full
+    rng = np.random.default_rng(70)
+    lens = [7, 40]
+    q_bits, kv_bits, qo, kvp, idx, _ = _rand_case(rng, 2, lens, permute=True)
+    ref = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16")
+    got = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16", page_size=1,
+                            kv_last_page_len=lens)
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------- several query tokens
+
+
+def _multi_token_case(rng, lens, q_lens):
+    B = len(lens)
+    total_q = int(sum(q_lens))
+    q_bits = torch.from_numpy(rng.standard_normal((total_q, 16, 576)).astype(np.float32)).to(
+        torch.bfloat16).view(torch.int16).numpy()
+    kv_bits = torch.from_numpy(rng.standard_normal((int(sum(lens)), 576)).astype(np.float32)).to(
+        torch.bfloat16).view(torch.int16).numpy()
+    qo = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    kvp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return q_bits, kv_bits, qo, kvp, np.arange(int(sum(lens)))
+
+
+def _sdpa_tokens(q_bits, kv_bits, t0, q_len, r0, n, is_causal):
+    Q = torch.from_numpy(q_bits[t0:t0 + q_len]).view(torch.bfloat16).to(torch.float64)  # [q, 16, 576]
+    K = torch.from_numpy(kv_bits[r0:r0 + n]).view(torch.bfloat16).to(torch.float64)
+    q4 = Q.permute(1, 0, 2)[None]  # [1, 16, q, 576]
+    k4 = K[None, None].expand(1, 16, n, 576)
+    v4 = K[:, :512][None, None].expand(1, 16, n, 512)
+    o = torch.nn.functional.scaled_dot_product_attention(q4, k4, v4, scale=1.0 / 24.0, is_causal=is_causal)
+    return o[0].permute(1, 0, 2).numpy()  # [q, 16, 512]
+
+
+def test_causal_prefill_equals_sdpa_is_causal():
+    # when every row of a sequence is also a query token (q_len = L), the causal rule is the
+    # square lower-triangular mask of scaled_dot_product_attention(is_causal=True)
+    rng = np.random.default_rng(80)
+    lens = [1, 5, 12]
+    q_bits, kv_bits, qo, kvp, idx = _multi_token_case(rng, lens, lens)
+    got = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16", causal=True)
+    for b, n in enumerate(lens):
+        ref = _sdpa_tokens(q_bits, kv_bits, qo[b], n, kvp[b], n, True)
+        assert np.max(np.abs(got[qo[b]:qo[b + 1]] - ref)) <= 1e-12
+
+
+def test_non_causal_tokens_equal_sdpa_without_mask():
+    rng = np.random.default_rng(81)
+    lens, q_lens = [9, 300], [3, 2]
+    q_bits, kv_bits, qo, kvp, idx = _multi_token_case(rng, lens, q_lens)
+    got = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16", causal=False)
+    for b in range(2):
+        ref = _sdpa_tokens(q_bits, kv_bits, qo[b], q_lens[b], kvp[b], lens[b], False)
+        assert np.max(np.abs(got[qo[b]:qo[b + 1]] - ref)) <= 1e-12
+
+
+def test_causal_token_sees_its_prefix():
+    # token i of q_len decodes over the first L - q_len + 1 + i rows; the last token sees all of them;
+    # tokens whose prefix is empty (L < q_len) give zeros
+    rng = np.random.default_rng(82)
+    lens, q_lens = [50, 2, 1], [4, 4, 3]
+    q_bits, kv_bits, qo, kvp, idx = _multi_token_case(rng, lens, q_lens)
+    got = oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16", causal=True)
+    for b, (L, ql) in enumerate(zip(lens, q_lens)):
+        for i in range(ql):
+            n = L - ql + 1 + i
+            t = qo[b] + i
+            if n <= 0:
+                assert np.array_equal(got[t], np.zeros((16, 512)))
+                continue
+            one = oracle.mla_decode(q_bits[t:t + 1], kv_bits, [0, 1], [kvp[b], kvp[b] + n], idx, q_dtype="bf16",
+                                    kv_dtype="bf16")
+            assert np.array_equal(got[t], one[0])
+    assert oracle.visible_rows(50, 4, 3, True) == 50 and oracle.visible_rows(50, 4, 0, True) == 47
+    assert oracle.visible_rows(2, 4, 1, True) == 0 and oracle.visible_rows(2, 4, 0, False) == 2
+
+
+# ------------------------------------------------------- amax-scaled Q cast
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+
+
+@pytest.mark.parametrize("mag", [1e-3, 1.0, 37.0, 3e4])
+def test_dynamic_q_cast_vs_torch(mag):
+    rng = np.random.default_rng(90)
+    bits = _bf16_bits(rng.standard_normal((3, 16, 576)) * mag)
+    codes, scale = oracle.quantize_q_dynamic(bits)
+    x = torch.from_numpy(bits).view(torch.bfloat16).to(torch.float32)
+    t_scale = x.abs().max() / torch.tensor(448.0, dtype=torch.float32)
+    t_codes = (x / t_scale).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.float32(scale) == t_scale.item()
+    assert np.array_equal(codes, t_codes)
+    # the largest magnitude lands on +-448 and the dequantised values stay within half an fp8 step
+    i = np.argmax(np.abs(x.numpy()))
+    assert codes.reshape(-1)[i] & 0x7F == 0x7E
+    deq = formats.decode_fp8_e4m3fn(codes) * scale
+    xv = x.numpy().astype(np.float64)
+    big = np.abs(xv) >= 2.0 ** -6 * scale
+    assert np.all(np.abs(deq - xv)[big] <= 2.0 ** -4 * np.abs(xv)[big] * (1 + 1e-6))
+
+
+def test_dynamic_q_cast_degenerate_inputs():
+    codes, scale = oracle.quantize_q_dynamic(_bf16_bits([0.0, -0.0, 0.0]))
+    assert scale == 1.0 and codes.tolist() == [0x00, 0x80, 0x00]
+    codes, scale = oracle.quantize_q_dynamic(np.zeros(0, dtype=np.int16))
+    assert scale == 1.0 and codes.size == 0
+    # non-finite values become the NaN code with their sign and do not enter the amax
+    bits = _bf16_bits([1.0, -2.0, 0.5]).copy()
+    bits = np.concatenate([bits, np.array([0x7F80, 0xFF80, 0x7FC1], dtype=np.uint16).view(np.int16)])
+    codes, scale = oracle.quantize_q_dynamic(bits)
+    assert np.float32(scale) == np.float32(2.0) / np.float32(448.0)
+    assert codes[3:].tolist() == [0x7F, 0xFF, 0x7F]
+    assert codes[1] == 0xFE  # -2 -> -448
