@@ -5,22 +5,34 @@
  * constants block and custom_kernel; submission 690201, the stage-1 and
  * reduce calls):
  *
- *   for every sequence b and its query token t = qo_indptr[b]:
- *     rows  j_i = kv_indices[i], i in [kv_indptr[b], kv_indptr[b+1])
+ *   for every sequence b, its query tokens t = qo_indptr[b] + tau and its
+ *   rows  j_0, j_1, ...  (page kv_indices[i], i in [kv_indptr[b], kv_indptr[b+1]),
+ *                         slot 0 .. page_size-1 of it; the last page holds
+ *                         kv_last_page_len[b] rows):
  *     s_i   = sm_scale * q_scale * kv_scale * sum_{d<576} q[t,h,d] * kv[j_i,d]
+ *             (then cap * tanh(s_i / cap) when params.logit_cap = cap > 0)
  *     out[t,h,e] = kv_scale * sum_i softmax(s)_i * kv[j_i,e]     (e < 512)
  *
- * for all 16 heads h.  The single latent KV head is 576 wide (512 latent +
- * 64 rope); V is the first 512 dims of the same row.  Pages hold one row
- * (page size 1), so a row index is a page index.
+ * for all 16 heads h, the softmax over the rows token tau sees: all of them,
+ * or with MLA_FLAG_CAUSAL the first n - q_len + 1 + tau of the sequence's n
+ * rows when it has q_len tokens.  The single latent KV head is 576 wide (512
+ * latent + 64 rope); V is the first 512 dims of the same row.  The pages' own
+ * calls use page size 1 and one token per sequence; pages of 2 and 8 rows,
+ * last-page lengths, q_seq_len, is_causal and logit_cap are the further
+ * arguments they pass (submissions 598454, 641982 and 689529).
  *
  * Layouts (all row-major, contiguous, device memory unless stated):
  *   q          [total_q, 16, 576]   bf16 or fp8 e4m3fn (bf16 also with fp8 q_dtype
  *                                   when MLA_FLAG_FUSED_Q_CAST is set)
- *   kv         [pool_rows, 576]     bf16 or fp8 e4m3fn (one KV head, page size 1)
+ *   kv         [pool_pages * page_size, 576]
+ *                                   bf16 or fp8 e4m3fn (one KV head); page p is
+ *                                   rows p*page_size .. p*page_size+page_size-1
  *   qo_indptr  [batch + 1]          int32, query rows of sequence b
- *   kv_indptr  [batch + 1]          int32, index positions of sequence b
- *   kv_indices [kv_indptr[batch]]   int32, pool row of each index position
+ *   kv_indptr  [batch + 1]          int32, index positions (pages) of sequence b
+ *   kv_indices [kv_indptr[batch]]   int32, pool page of each index position
+ *   kv_last_page_len [batch]        int32, rows in each sequence's last page
+ *                                   (mla_decode_run_paged only; values are
+ *                                   clamped into [1, page_size])
  *   out        [total_q, 16, 512]   bf16
  *   q_scale, kv_scale               one float32 each, in device memory
  *                                   (read only for fp8 operands; may be NULL
@@ -38,8 +50,9 @@
  * Errors: every entry point returns mla_status.  Arguments are validated on
  * the host before any HIP call; a rejected call enqueues nothing.  A HIP
  * launch failure is reported as MLA_ERR_HIP.  Index values (kv_indices,
- * qo_indptr) are not checked on the device: out-of-range values are a caller
- * error and lead to undefined results.
+ * qo_indptr, kv_last_page_len) are not checked on the device: out-of-range
+ * values are a caller error and lead to undefined results.  Pool rows
+ * (page * page_size + slot) must fit in int32.
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H
@@ -53,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 1
+#define MLA_DECODE_ABI_VERSION 2
 
 typedef enum {
   MLA_OK = 0,
@@ -76,20 +89,24 @@ typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP8_E4M3FN = 1 } mla_dtype;
                                     the attention kernel casts them to fp8
                                     e4m3fn itself, bit-identically to
                                     mla_decode_quantize_q (saves its launch) */
+#define MLA_FLAG_CAUSAL 4u /* several query tokens per sequence: token tau of q_len
+                              sees the sequence's first n - q_len + 1 + tau rows
+                              (submission 689529 builds its metadata with
+                              is_causal set) */
 
 /*
  * Problem description.  The fixed fields restate the model constants of
- * submission 689529 (16 heads, 1 KV head, 576 / 512 dims, page size 1);
- * anything else is MLA_ERR_UNSUPPORTED.
+ * submission 689529 (16 heads, 1 KV head, 576 / 512 dims); anything else is
+ * MLA_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t batch;        /* sequences, >= 1 */
-  int32_t total_q;      /* query rows; must equal batch (one decode token per sequence) */
+  int32_t total_q;      /* query rows, in [batch, batch * max_q_len] */
   int32_t num_heads;    /* 16 */
   int32_t num_kv_heads; /* 1 */
   int32_t qk_dim;       /* 576 */
   int32_t v_dim;        /* 512 */
-  int32_t page_size;    /* 1 */
+  int32_t page_size;    /* rows per page: a power of two, 1 .. 1024 */
   int32_t q_dtype;      /* mla_dtype */
   int32_t kv_dtype;     /* mla_dtype */
   int32_t num_units;    /* 0 = the device's compute-unit count.  Upper bound on the
@@ -98,6 +115,11 @@ typedef struct {
   int32_t min_chunk;    /* 0 = default (256).  Smallest share of KV rows per workgroup;
                            must be a multiple of 32 when set. */
   uint32_t flags;       /* MLA_FLAG_* */
+  int32_t max_q_len;    /* 0 = 1.  Most query tokens of one sequence (qo_indptr[b+1] -
+                           qo_indptr[b]), at most 16.  Tokens past it are not
+                           computed.  With more than one, each KV tile the
+                           kernel reads serves two tokens at once. */
+  float logit_cap;      /* 0 = off; > 0: scores pass through cap * tanh(s / cap) */
 } mla_decode_params;
 
 /*
@@ -114,8 +136,8 @@ typedef struct {
   int32_t device;
   int32_t reserved;
   uint64_t off_counters; /* int32 [batch]: arrivals per split sequence (fused merge), left at 0 after each run */
-  uint64_t off_part_o;   /* float32 [2 * num_units, 16, 512]: normalised split partials */
-  uint64_t off_part_lse; /* float32 [2 * num_units, 16]: log2-sum-exp of each partial */
+  uint64_t off_part_o;   /* float32 [2 * num_units * max_q_len, 16, 512]: normalised split partials */
+  uint64_t off_part_lse; /* float32 [2 * num_units * max_q_len, 16]: log2-sum-exp of each partial */
 } mla_decode_plan_t;
 
 /* Bytes of device workspace mla_decode_plan needs for these params; 0 if the
@@ -137,13 +159,25 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
  * chosen on the device from kv_indptr; sequences split over several
  * workgroups are merged by a second launch (or, with MLA_FLAG_FUSED_MERGE, by
  * the last arriving workgroup).  Pointers as in the layout table above;
- * sm_scale is a host float (1/sqrt(576) in the pages).  Sequences with no KV
- * rows produce zeros.
+ * sm_scale is a host float (1/sqrt(576) in the pages).  Every page is full
+ * (see mla_decode_run_paged).  Sequences with no KV rows, and causal tokens
+ * that see no row, produce zeros.
  */
 mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv,
                           const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                           const float* q_scale, const float* kv_scale, float sm_scale, void* out,
                           hipStream_t stream);
+
+/*
+ * mla_decode_run with the rows of each sequence's last page given by
+ * kv_last_page_len[b] (device int32 [batch], clamped into [1, page_size];
+ * NULL: every page full), as the pages pass kv_last_page_lens next to
+ * kv_indptr in pages (submissions 598454 and 641982, pages of 2 and 8 rows).
+ */
+mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, const void* kv,
+                                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
+                                float sm_scale, void* out, hipStream_t stream);
 
 /*
  * Step a0 for fp8 queries: cast n bf16 values to fp8 e4m3fn with

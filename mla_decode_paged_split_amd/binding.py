@@ -24,6 +24,7 @@ __all__ = [
     "MLA_DTYPE_FP8_E4M3FN",
     "MLA_FLAG_FUSED_MERGE",
     "MLA_FLAG_FUSED_Q_CAST",
+    "MLA_FLAG_CAUSAL",
     "MlaDecodeParams",
     "MlaDecodePlan",
     "library_path",
@@ -33,6 +34,7 @@ __all__ = [
     "mla_decode_workspace_size",
     "mla_decode_plan",
     "mla_decode_run",
+    "mla_decode_run_paged",
     "mla_decode_quantize_q",
     "mla_decode_reduce",
     "make_params",
@@ -48,6 +50,7 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP8_E4M3FN = 1
 MLA_FLAG_FUSED_MERGE = 1
 MLA_FLAG_FUSED_Q_CAST = 2
+MLA_FLAG_CAUSAL = 4
 
 _DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3FN}
 
@@ -66,6 +69,8 @@ class MlaDecodeParams(ctypes.Structure):
         ("num_units", ctypes.c_int32),
         ("min_chunk", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("max_q_len", ctypes.c_int32),
+        ("logit_cap", ctypes.c_float),
     ]
 
 
@@ -108,6 +113,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_plan.restype = ctypes.c_int
         L.mla_decode_run.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
         L.mla_decode_run.restype = ctypes.c_int
+        L.mla_decode_run_paged.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
+                                           vp]
+        L.mla_decode_run_paged.restype = ctypes.c_int
         L.mla_decode_quantize_q.argtypes = [vp, vp, i64, vp]
         L.mla_decode_quantize_q.restype = ctypes.c_int
         L.mla_decode_reduce.argtypes = [vp, vp, vp, i32, vp, vp]
@@ -157,12 +165,13 @@ def mla_decode_abi_version() -> int:
 
 def make_params(batch: int, q_dtype: str, kv_dtype: str, *, total_q: Optional[int] = None, num_units: int = 0,
                 min_chunk: int = 0, flags: int = 0, num_heads: int = 16, num_kv_heads: int = 1, qk_dim: int = 576,
-                v_dim: int = 512, page_size: int = 1) -> MlaDecodeParams:
+                v_dim: int = 512, page_size: int = 1, max_q_len: int = 0, logit_cap: float = 0.0) -> MlaDecodeParams:
     return MlaDecodeParams(
         batch=batch, total_q=batch if total_q is None else total_q, num_heads=num_heads, num_kv_heads=num_kv_heads,
-        qk_dim=qk_dim, v_dim=v_dim, page_size=page_size, q_dtype=_DTYPES.get(q_dtype, q_dtype) if isinstance(q_dtype, str) else q_dtype,
+        qk_dim=qk_dim, v_dim=v_dim, page_size=page_size,
+        q_dtype=_DTYPES.get(q_dtype, q_dtype) if isinstance(q_dtype, str) else q_dtype,
         kv_dtype=_DTYPES.get(kv_dtype, kv_dtype) if isinstance(kv_dtype, str) else kv_dtype,
-        num_units=num_units, min_chunk=min_chunk, flags=flags,
+        num_units=num_units, min_chunk=min_chunk, flags=flags, max_q_len=max_q_len, logit_cap=logit_cap,
     )
 
 
@@ -178,18 +187,34 @@ def mla_decode_plan(params: MlaDecodeParams, workspace: torch.Tensor, stream=Non
     return plan
 
 
-def mla_decode_run(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
-                   kv_indptr: torch.Tensor, kv_indices: torch.Tensor, q_scale: Optional[torch.Tensor],
-                   kv_scale: Optional[torch.Tensor], sm_scale: float, out: torch.Tensor, stream=None) -> None:
-    for name, t in (("qo_indptr", qo_indptr), ("kv_indptr", kv_indptr), ("kv_indices", kv_indices)):
-        if t.dtype != torch.int32:
+def _check_index_args(out, **ints) -> None:
+    for name, t in ints.items():
+        if t is not None and t.dtype != torch.int32:
             raise ValueError(f"{name} must be int32")
     if out.dtype != torch.bfloat16:
         raise ValueError("out must be bf16")
+
+
+def mla_decode_run(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
+                   kv_indptr: torch.Tensor, kv_indices: torch.Tensor, q_scale: Optional[torch.Tensor],
+                   kv_scale: Optional[torch.Tensor], sm_scale: float, out: torch.Tensor, stream=None) -> None:
+    _check_index_args(out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices)
     code = lib().mla_decode_run(ctypes.byref(plan), _ptr(q), _ptr(kv), _ptr(qo_indptr), _ptr(kv_indptr),
                                 _ptr(kv_indices), _ptr(q_scale), _ptr(kv_scale), float(sm_scale), _ptr(out),
                                 _stream(stream))
     _check(code, "mla_decode_run")
+
+
+def mla_decode_run_paged(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
+                         kv_indptr: torch.Tensor, kv_indices: torch.Tensor, kv_last_page_len: Optional[torch.Tensor],
+                         q_scale: Optional[torch.Tensor], kv_scale: Optional[torch.Tensor], sm_scale: float,
+                         out: torch.Tensor, stream=None) -> None:
+    _check_index_args(out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                      kv_last_page_len=kv_last_page_len)
+    code = lib().mla_decode_run_paged(ctypes.byref(plan), _ptr(q), _ptr(kv), _ptr(qo_indptr), _ptr(kv_indptr),
+                                      _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(q_scale), _ptr(kv_scale),
+                                      float(sm_scale), _ptr(out), _stream(stream))
+    _check(code, "mla_decode_run_paged")
 
 
 def mla_decode_quantize_q(q_bf16: torch.Tensor, q_fp8: torch.Tensor, stream=None) -> None:
@@ -213,8 +238,10 @@ class Decoder:
     """Owns one workspace and plan for a (batch, dtype pair); run() is one decode step."""
 
     def __init__(self, batch: int, q_dtype: str, kv_dtype: str, device: torch.device | str = "cuda", *,
-                 num_units: int = 0, min_chunk: int = 0, flags: int = 0, stream=None):
-        self.params = make_params(batch, q_dtype, kv_dtype, num_units=num_units, min_chunk=min_chunk, flags=flags)
+                 num_units: int = 0, min_chunk: int = 0, flags: int = 0, page_size: int = 1, max_q_len: int = 0,
+                 total_q: Optional[int] = None, logit_cap: float = 0.0, stream=None):
+        self.params = make_params(batch, q_dtype, kv_dtype, num_units=num_units, min_chunk=min_chunk, flags=flags,
+                                  page_size=page_size, max_q_len=max_q_len, total_q=total_q, logit_cap=logit_cap)
         nbytes = mla_decode_workspace_size(self.params)
         if nbytes == 0:
             raise RuntimeError("mla_decode_workspace_size rejected the parameters")
@@ -223,6 +250,12 @@ class Decoder:
         self.q_dtype = q_dtype
         self.kv_dtype = kv_dtype
 
-    def run(self, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out, stream=None):
-        mla_decode_run(self.plan, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out, stream)
+    def run(self, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out, stream=None,
+            kv_last_page_len=None):
+        if kv_last_page_len is None:
+            mla_decode_run(self.plan, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out,
+                           stream)
+        else:
+            mla_decode_run_paged(self.plan, q, kv, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_scale,
+                                 kv_scale, sm_scale, out, stream)
         return out

@@ -16,7 +16,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kDefaultMinChunk = 256;
-constexpr uint32_t kKnownFlags = MLA_FLAG_FUSED_MERGE | MLA_FLAG_FUSED_Q_CAST;
+constexpr int kMaxPageSize = 1024;
+constexpr int kMaxQLen = 16;
+constexpr uint32_t kKnownFlags = MLA_FLAG_FUSED_MERGE | MLA_FLAG_FUSED_Q_CAST | MLA_FLAG_CAUSAL;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -32,11 +34,15 @@ mla_status validate_params(const mla_decode_params* p) {
   if ((p->flags & ~kKnownFlags) != 0u) return MLA_ERR_INVALID_ARG;
   if (p->min_chunk != 0 && p->min_chunk % mla::kSplitAlign != 0) return MLA_ERR_INVALID_ARG;
   if (p->v_dim > p->qk_dim) return MLA_ERR_INVALID_ARG;
+  if (p->max_q_len < 0) return MLA_ERR_INVALID_ARG;
+  if (!(p->logit_cap >= 0.0f) || p->logit_cap == INFINITY) return MLA_ERR_INVALID_ARG;
   // the model constants the kernels are written for
-  if (p->num_heads != mla::kHeads || p->num_kv_heads != 1 || p->qk_dim != mla::kQKDim || p->v_dim != mla::kVDim ||
-      p->page_size != 1)
+  if (p->num_heads != mla::kHeads || p->num_kv_heads != 1 || p->qk_dim != mla::kQKDim || p->v_dim != mla::kVDim)
     return MLA_ERR_UNSUPPORTED;
-  if (p->total_q != p->batch) return MLA_ERR_UNSUPPORTED;  // one decode token per sequence
+  if (p->page_size > kMaxPageSize || (p->page_size & (p->page_size - 1)) != 0) return MLA_ERR_UNSUPPORTED;
+  if (p->max_q_len > kMaxQLen) return MLA_ERR_UNSUPPORTED;
+  const int64_t max_q = p->max_q_len > 0 ? p->max_q_len : 1;
+  if (p->total_q < p->batch || p->total_q > (int64_t)p->batch * max_q) return MLA_ERR_INVALID_ARG;
   if (p->q_dtype == MLA_DTYPE_FP8_E4M3FN && p->kv_dtype == MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
   if ((p->flags & MLA_FLAG_FUSED_Q_CAST) && p->q_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_INVALID_ARG;
   if (p->num_units > (1 << 20)) return MLA_ERR_UNSUPPORTED;
@@ -62,22 +68,49 @@ struct Layout {
   size_t counters, part_o, part_lse, total;
 };
 
-Layout layout_for(int32_t batch, int32_t units) {
+int32_t max_q_of(const mla_decode_params* p) { return p->max_q_len > 0 ? p->max_q_len : 1; }
+
+// Partials: two slots per workgroup share, each with a row per query token.
+Layout layout_for(const mla_decode_params* p, int32_t units) {
+  const size_t slots = (size_t)2 * units * max_q_of(p);
   Layout L;
   L.counters = 0;
-  L.part_o = align_up((size_t)batch * sizeof(int32_t));
-  L.part_lse = L.part_o + align_up((size_t)2 * units * mla::kHeads * mla::kVDim * sizeof(float));
-  L.total = L.part_lse + align_up((size_t)2 * units * mla::kHeads * sizeof(float));
+  L.part_o = align_up((size_t)p->batch * sizeof(int32_t));
+  L.part_lse = L.part_o + align_up(slots * mla::kHeads * mla::kVDim * sizeof(float));
+  L.total = L.part_lse + align_up(slots * mla::kHeads * sizeof(float));
   return L;
 }
 
+int ilog2(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+// QL query tokens per walk of a piece; batches beyond the kernel's LDS
+// sequence table read the indptrs from memory.
+template <mla::Dt QT, mla::Dt KT, int QL, bool kGeneral>
+hipError_t launch_attention_ql(const mla::Args& a, hipStream_t stream) {
+  if (a.batch <= mla::kSeqTable)
+    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, false, QL, kGeneral>), dim3(a.units), dim3(mla::kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, true, QL, kGeneral>), dim3(a.units), dim3(mla::kThreads), 0,
+                       stream, a);
+  return hipGetLastError();
+}
+
+// The plain decode (pages of one row, one token per sequence, no soft-cap)
+// runs a kernel with the page arithmetic and the cap compiled out.  Otherwise
+// fp8 KV serves two tokens per walk of a piece and bf16 KV (twice the row
+// bytes in the register ring) walks a piece once per token.
 template <mla::Dt QT, mla::Dt KT>
 hipError_t launch_attention(const mla::Args& a, hipStream_t stream) {
-  if (a.batch <= mla::kSeqTable)
-    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, false>), dim3(a.units), dim3(mla::kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, true>), dim3(a.units), dim3(mla::kThreads), 0, stream, a);
-  return hipGetLastError();
+  const bool general = a.page_shift > 0 || a.max_q_len > 1 || a.logit_cap > 0.f;
+  if (!general) return launch_attention_ql<QT, KT, 1, false>(a, stream);
+  if constexpr (KT == mla::Dt::FP8)
+    if (a.max_q_len > 1) return launch_attention_ql<QT, KT, 2, true>(a, stream);
+  return launch_attention_ql<QT, KT, 1, true>(a, stream);
 }
 
 }  // namespace
@@ -109,7 +142,7 @@ size_t mla_decode_workspace_size(const mla_decode_params* params) {
     int32_t device = 0;
     if (resolve_units(params, &units, &device) != MLA_OK) return 0;
   }
-  return layout_for(params->batch, units).total;
+  return layout_for(params, units).total;
 }
 
 mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, size_t workspace_bytes,
@@ -119,12 +152,12 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
   if (plan == nullptr) return MLA_ERR_INVALID_ARG;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MLA_ERR_WORKSPACE;
   // the sizes that do not need the device are checked before any HIP call
-  if (params->num_units > 0 && workspace_bytes < layout_for(params->batch, params->num_units).total)
+  if (params->num_units > 0 && workspace_bytes < layout_for(params, params->num_units).total)
     return MLA_ERR_WORKSPACE;
   int32_t units = 0, device = 0;
   st = resolve_units(params, &units, &device);
   if (st != MLA_OK) return st;
-  const Layout L = layout_for(params->batch, units);
+  const Layout L = layout_for(params, units);
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
 
   mla_decode_plan_t pl;
@@ -132,6 +165,7 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
   pl.params = *params;
   pl.params.num_units = units;
   pl.params.min_chunk = params->min_chunk > 0 ? params->min_chunk : kDefaultMinChunk;
+  pl.params.max_q_len = max_q_of(params);
   pl.workspace = workspace;
   pl.workspace_bytes = workspace_bytes;
   pl.device = device;
@@ -147,15 +181,16 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
   return MLA_OK;
 }
 
-mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,
-                          const int32_t* kv_indptr, const int32_t* kv_indices, const float* q_scale,
-                          const float* kv_scale, float sm_scale, void* out, hipStream_t stream) {
+mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, const void* kv,
+                                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
+                                float sm_scale, void* out, hipStream_t stream) {
   if (plan == nullptr) return MLA_ERR_INVALID_ARG;
   const mla_decode_params& p = plan->params;
   mla_status st = validate_params(&p);
   if (st != MLA_OK) return st;
   if (p.num_units < 1 || p.min_chunk < mla::kSplitAlign) return MLA_ERR_INVALID_ARG;
-  if (plan->workspace == nullptr || plan->workspace_bytes < layout_for(p.batch, p.num_units).total)
+  if (plan->workspace == nullptr || plan->workspace_bytes < layout_for(&p, p.num_units).total)
     return MLA_ERR_WORKSPACE;
   if (q == nullptr || kv == nullptr || qo_indptr == nullptr || kv_indptr == nullptr || kv_indices == nullptr ||
       out == nullptr)
@@ -171,9 +206,11 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
   a.qo_indptr = qo_indptr;
   a.kv_indptr = kv_indptr;
   a.kv_indices = kv_indices;
+  a.kv_last_page_len = kv_last_page_len;
   a.q_scale = q_scale;
   a.kv_scale = kv_scale;
   a.sm_scale = sm_scale;
+  a.logit_cap = p.logit_cap;
   a.out = static_cast<uint16_t*>(out);
   a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
   a.part_lse = reinterpret_cast<float*>(ws + plan->off_part_lse);
@@ -181,6 +218,9 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
   a.batch = p.batch;
   a.units = p.num_units;
   a.min_chunk = p.min_chunk;
+  a.page_shift = ilog2(p.page_size);
+  a.max_q_len = max_q_of(&p);
+  a.causal = (p.flags & MLA_FLAG_CAUSAL) ? 1 : 0;
   a.fused = (p.flags & MLA_FLAG_FUSED_MERGE) ? 1 : 0;
   a.q_cast = (p.flags & MLA_FLAG_FUSED_Q_CAST) ? 1 : 0;
 
@@ -193,10 +233,18 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
     err = launch_attention<mla::Dt::FP8, mla::Dt::FP8>(a, stream);
   if (err != hipSuccess) return MLA_ERR_HIP;
   if (!a.fused) {
-    hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(p.batch, mla::kHeads), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(p.batch, mla::kHeads, a.max_q_len), dim3(64), 0, stream,
+                       a);
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   }
   return MLA_OK;
+}
+
+mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,
+                          const int32_t* kv_indptr, const int32_t* kv_indices, const float* q_scale,
+                          const float* kv_scale, float sm_scale, void* out, hipStream_t stream) {
+  return mla_decode_run_paged(plan, q, kv, qo_indptr, kv_indptr, kv_indices, nullptr, q_scale, kv_scale, sm_scale,
+                              out, stream);
 }
 
 mla_status mla_decode_quantize_q(const void* q_bf16, void* q_fp8, int64_t n, hipStream_t stream) {

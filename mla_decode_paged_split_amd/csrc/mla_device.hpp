@@ -93,15 +93,13 @@ struct KvLayout<Dt::BF16> {
 };
 
 
-template <Dt KV>
+template <Dt KV, int QL>
 struct alignas(16) Smem {
-  union {
-    uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];  // V part of the current / next tile
-  };
-  u32x2_t p[2][kWaves][64];   // bf16 weights: wave, lane -> 4 rows of one head
-  float mx[2][kWaves][kHeads];  // per-wave tile max of each head
-  float lsum[kWaves][kHeads];
-  int seq[kSeqTable][3];  // kv_indptr[b], kv_indptr[b+1], qo_indptr[b] of the first kSeqTable sequences
+  uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];  // V part of the current / next tile
+  u32x2_t p[2][QL][kWaves][64];     // bf16 weights: token, wave, lane -> 4 rows of one head
+  float mx[2][kWaves][QL][kHeads];  // per-wave tile max of each token and head
+  float lsum[kWaves][QL][kHeads];
+  int seq[kSeqTable][4];  // kv_indptr[b], kv_indptr[b+1], qo_indptr[b], (tokens << 16) | last-page rows
   int bmin;
   int bmax;
   int arrive;
@@ -113,16 +111,21 @@ struct Args {
   const int32_t* qo_indptr;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
+  const int32_t* kv_last_page_len;  // [batch] rows in each sequence's last page, or null: pages full
   const float* q_scale;
   const float* kv_scale;
   float sm_scale;
+  float logit_cap;    // 0: off
   uint16_t* out;      // bf16 bits [total_q, 16, 512]
-  float* part_o;      // [2*units, 16, 512]
-  float* part_lse;    // [2*units, 16], log2 domain
+  float* part_o;      // [2*units*max_q_len, 16, 512]
+  float* part_lse;    // [2*units*max_q_len, 16], log2 domain
   int32_t* counters;  // [batch]
   int32_t batch;
   int32_t units;
-  int32_t min_chunk;
+  int32_t min_chunk;  // rows
+  int32_t page_shift;  // log2(page size)
+  int32_t max_q_len;   // query tokens per sequence at most
+  int32_t causal;
   int32_t fused;
   int32_t q_cast;  // fp8 Q given as bf16: cast in the kernel (same rounding as mla_quantize_q_kernel)
 };
@@ -208,15 +211,14 @@ __device__ __forceinline__ uint32_t bf16_to_e4m3fn(uint32_t x) {
   return sign | n;  // n == 8 is the smallest normal, encoded the same way
 }
 
-// Eight bf16 Q values (four dwords) -> eight e4m3fn bytes with the same
-// rounding as bf16_to_e4m3fn.  The hardware conversion (low-word form, scale
-// 1) agrees with it on every non-NaN input; it gives a positive NaN the
-// negative NaN code, so a lane whose values hold a positive NaN redoes the
-// cast bit by bit.  Each pair is converted into the low word of a fresh
-// register and the pairs are joined with shifts.  The pair goes through a
-// named scalar: hipcc lowers __builtin_bit_cast of an ext-vector subscript
-// to element 0 whatever the index.
-__device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w, uint32_t& posnan) {
+// Eight bf16 Q values (four dwords) -> eight e4m3fn bytes, bit-identical to
+// bf16_to_e4m3fn on each value.  The hardware conversion (low-word form,
+// scale 1) agrees with it on every input except a positive NaN, to which it
+// gives the negative NaN code; those bytes are patched to 0x7F without a
+// branch.  Each pair goes through a named scalar: hipcc lowers
+// __builtin_bit_cast of an ext-vector subscript to element 0 whatever the
+// index.
+__device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w) {
   typedef short short2v __attribute__((ext_vector_type(2)));
   uint32_t p[4];
 #pragma unroll
@@ -224,42 +226,36 @@ __device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w, uint32_t& posnan
     const uint32_t pair = w[i];
     const short2v o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(short2v{0, 0}, __builtin_bit_cast(bf16x2_t, pair),
                                                                 1.0f, false);
-    p[i] = __builtin_bit_cast(uint32_t, o) & 0xFFFFu;
+    // bit 15 / 31 set where a half is a positive NaN: (h & 0x7fff) + 0x7f carries into bit 15, sign clear
+    const uint32_t pn = ((pair & 0x7fff7fffu) + 0x007f007fu) & ~pair & 0x80008000u;
+    const uint32_t fix = ((pn >> 15) & 1u) * 0xFFu | ((pn >> 31) * 0xFF00u);
+    p[i] = ((__builtin_bit_cast(uint32_t, o) & 0xFFFFu) & ~fix) | (0x7F7Fu & fix);
   }
-  const uint32_t r[2] = {p[0] | (p[1] << 16), p[2] | (p[3] << 16)};
-  // a half h is a NaN iff (h & 0x7fff) + 0x7f carries into bit 15; positive iff its sign bit is clear
-#pragma unroll
-  for (int i = 0; i < 4; ++i) posnan |= ((w[i] & 0x7fff7fffu) + 0x007f007fu) & ~w[i] & 0x80008000u;
-  return (uint64_t)r[0] | ((uint64_t)r[1] << 32);
-}
-
-__device__ __forceinline__ uint64_t bf16x8_to_e4m3fn_exact(u32x4_t w) {
-  uint64_t out = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t lo = bf16_to_e4m3fn(w[i] & 0xFFFFu);
-    const uint64_t hi = bf16_to_e4m3fn(w[i] >> 16);
-    out |= (lo | (hi << 8)) << (16 * i);
-  }
-  return out;
+  return (uint64_t)(p[0] | (p[1] << 16)) | ((uint64_t)(p[2] | (p[3] << 16)) << 32);
 }
 
 // ---------------------------------------------------------------- partition
 
+// The split works on index positions (pages): a share of C positions holds
+// C pages, i.e. C * page_size rows except where a sequence's last page is
+// part-filled.  C is a multiple of max(1, 32 / page_size) and at least
+// min_chunk rows' worth of pages.
 struct Geo {
   int32_t base;   // kv_indptr[0]
-  int32_t total;  // N rows over all sequences
-  int32_t chunk;  // C rows per workgroup share
+  int32_t total;  // N index positions over all sequences
+  int32_t chunk;  // C positions per workgroup share
   int32_t n_wg;   // shares in use (>= 1)
 };
 
-__device__ __forceinline__ Geo make_geo(const int32_t* kv_indptr, int batch, int units, int min_chunk) {
+__device__ __forceinline__ Geo make_geo(const int32_t* kv_indptr, int batch, int units, int min_chunk, int sh) {
   Geo g;
   g.base = kv_indptr[0];
   g.total = kv_indptr[batch] - g.base;
+  const int align = max(1, kSplitAlign >> sh);
+  const int min_pos = max(1, min_chunk >> sh);
   int64_t c = ((int64_t)g.total + units - 1) / units;
-  c = (c + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
-  if (c < min_chunk) c = min_chunk;
+  c = (c + align - 1) / align * align;
+  if (c < min_pos) c = min_pos;
   g.chunk = (int32_t)c;
   int64_t n = ((int64_t)g.total + c - 1) / c;
   g.n_wg = n < 1 ? 1 : (int32_t)n;
@@ -363,135 +359,190 @@ __device__ __forceinline__ void zero_row_by_thread(uint16_t* out_row) {
 
 // --------------------------------------------------------------- one piece
 
+// Row `pr` of a piece that starts at index position ip0 and has nrows rows
+// lives in page kv_indices[ip0 + pr / page_size], slot pr % page_size
+// (page_size = 2^sh), i.e. pool row page * page_size + slot.  Rows at or past
+// nrows stand for the piece's first row instead, which is always valid.
+// The page load and the row composition are separate so that the ring can
+// keep the raw page index in flight and compose the row only when it issues
+// the tile's loads (using a loaded value at once would wait for it).
+__device__ __forceinline__ int piece_page(const int32_t* __restrict__ kv_indices, int ip0, int nrows, int pr,
+                                          int sh) {
+  return kv_indices[ip0 + ((pr < nrows ? pr : 0) >> sh)];
+}
+
+__device__ __forceinline__ int page_row(int page, int nrows, int pr, int sh) {
+  return (page << sh) | ((pr < nrows ? pr : 0) & ((1 << sh) - 1));
+}
+
 // The register ring of one piece: the rows of D tiles in flight (tile t in
 // slot t % D) and the row indices of the next D tiles.  Lane (c16, g) of wave
 // w owns row 16w + c16 of every 64-row tile and 16-byte chunks 4j + g of it.
-template <Dt KT>
+// Tiles in flight per wave: the layout's depth, one less when two tokens of
+// bf16 Q (72 more registers per token) share the walk.
+template <Dt QT, Dt KT, int QL>
+constexpr int ring_depth() {
+  return (QL > 1 && QT == Dt::BF16) ? KvLayout<KT>::kDepth - 1 : KvLayout<KT>::kDepth;
+}
+
+template <Dt KT, int Depth>
 struct Ring {
-  static constexpr int D = KvLayout<KT>::kDepth;
+  static constexpr int D = Depth;
   u32x4_t dat[D][KvLayout<KT>::kChunks];
-  int first[D];  // rows of tiles 0..D-1
-  int next[D];   // rows of tiles D..2D-1, then of each slot's next refill
+  int first[D];  // pages of tiles 0..D-1
+  int next[D];   // pages of tiles D..2D-1, then of each slot's next refill
 };
 
-// Fetch the ring's starting indices for a piece beginning at index position
-// ip0.  Positions at or past ip_end read the piece's first index instead
-// (always a valid position).
-template <Dt KT>
-__device__ __forceinline__ void issue_ring_indices(const int32_t* __restrict__ kv_indices, int ip0, int ip_end,
-                                                   Ring<KT>& r) {
-  constexpr int D = Ring<KT>::D;
+// Fetch the ring's starting page indices for a piece of nrows rows beginning
+// at index position ip0.
+template <class R>
+__device__ __forceinline__ void issue_ring_indices(const int32_t* __restrict__ kv_indices, int ip0, int nrows,
+                                                   int sh, R& r) {
+  constexpr int D = R::D;
   const int my_row = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15);
 #pragma unroll
-  for (int k = 0; k < D; ++k) {
-    const int p = ip0 + k * kTileRows + my_row;
-    r.first[k] = kv_indices[p < ip_end ? p : ip0];
-  }
+  for (int k = 0; k < D; ++k) r.first[k] = piece_page(kv_indices, ip0, nrows, k * kTileRows + my_row, sh);
 #pragma unroll
-  for (int k = 0; k < D; ++k) {
-    const int p = ip0 + (k + D) * kTileRows + my_row;
-    r.next[k] = kv_indices[p < ip_end ? p : ip0];
-  }
+  for (int k = 0; k < D; ++k) r.next[k] = piece_page(kv_indices, ip0, nrows, (k + D) * kTileRows + my_row, sh);
 }
 
 // Start the loads of the ring's first D tiles (in the steady state's slot
 // order, kept by scheduling barriers so the loop's wait counts stay exact).
-template <Dt KT>
-__device__ __forceinline__ void issue_ring_rows(const void* kv, Ring<KT>& r) {
+template <Dt KT, class R>
+__device__ __forceinline__ void issue_ring_rows(const void* kv, int nrows, int sh, R& r) {
   using L = KvLayout<KT>;
-  constexpr int D = Ring<KT>::D;
+  constexpr int D = R::D;
   const int g = (threadIdx.x & 63) >> 4;
+  const int my_row = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < D; ++k) {
-    const uint8_t* row = reinterpret_cast<const uint8_t*>(kv) + (size_t)r.first[k] * L::kRowBytes + g * 16;
+    const int row = page_row(r.first[k], nrows, k * kTileRows + my_row, sh);
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(kv) + (size_t)row * L::kRowBytes + g * 16;
 #pragma unroll
-    for (int j = 0; j < L::kChunks; ++j) r.dat[k][j] = *reinterpret_cast<const u32x4_t*>(row + j * 64);
+    for (int j = 0; j < L::kChunks; ++j) r.dat[k][j] = *reinterpret_cast<const u32x4_t*>(src + j * 64);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Attention of one query row over the index positions [ip0, ip1) (one piece
-// of one sequence).  All 256 threads take part; the workgroup writes either
-// the final bf16 row (complete) or the float32 partial in `slot`.
-template <Dt QT, Dt KT>
-__device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip1, bool complete, int slot,
-                             float c_score, float out_mul, Ring<KT>& ring) {
+// One pass over a piece: its rows, the query tokens it serves in this pass
+// and where their results go.
+template <int QL>
+struct Piece {
+  int ip0;        // first index position
+  int nrows;      // rows of the piece
+  int t0;         // query row of the pass's first token
+  int ntok;       // tokens in this pass, 1..QL
+  int lim[QL];    // rows (from the piece start) token j sees: <= nrows, <= 0 for none
+  int slot;       // partial row of token j is slot + j (unused when complete)
+  bool complete;  // the piece is the whole sequence: write bf16 rows
+};
+
+// Score transform, raw dot product -> log2-domain logit: sc * c_score, or
+// with the soft-cap cap * tanh(sc * c_nat / cap) * log2(e), computed as
+// k2 * (1 - 2 / (2^(k1 sc) + 1)) with k1 = 2 log2(e) c_nat / cap and
+// k2 = cap log2(e) (the limits +-1 come out exactly when 2^(k1 sc)
+// overflows or underflows).
+struct Logit {
+  float c_score;
+  float k1;
+  float k2;
+  int capped;  // workgroup-uniform: decided once per tile, not per score
+  template <bool kGeneral>
+  __device__ __forceinline__ void apply(const f32x4_t& sc, float (&y)[4]) const {
+    if (kGeneral && capped) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = fast_exp2(sc[i] * k1);
+        y[i] = k2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = sc[i] * c_score;
+    }
+  }
+};
+
+// Attention of the pass's query tokens over the rows of one piece.  All 256
+// threads take part; the workgroup writes either the final bf16 rows
+// (complete) or the float32 partials.  kGeneral = false is the plain decode
+// (pages of one row, no soft-cap), with both compiled out of the loop.
+template <Dt QT, Dt KT, int QL, bool kGeneral, class RingT>
+__device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& pc, const Logit logit,
+                             float out_mul, RingT& ring) {
   using L = KvLayout<KT>;
-  constexpr int D = L::kDepth;
+  constexpr int D = RingT::D;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int g = lane >> 4;
+  const int sh = kGeneral ? a.page_shift : 0;
 
   // Q as the B operand of S^T = K . Q^T (lane holds head c16).  A k-step takes
   // 8 values per lane; for fp8 KV a 16-byte chunk feeds two k-steps, for bf16
-  // KV one.  Q is read with the same d mapping as the K chunks.
+  // KV one.  Q is read with the same d mapping as the K chunks.  Tokens past
+  // ntok read the first token's row (their results are never written).
   constexpr int kSteps = kQKDim / 32;  // 18
-  bf16x8_t qb[QT == Dt::BF16 ? kSteps : 1];
-  uint64_t q8[QT == Dt::FP8 ? kSteps : 1];
+  bf16x8_t qb[QL][QT == Dt::BF16 ? kSteps : 1];
+  uint64_t q8[QL][QT == Dt::FP8 ? kSteps : 1];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int d0 = (KT == Dt::FP8) ? (((s >> 1) * 4 + g) * 16 + (s & 1) * 8) : ((s * 4 + g) * 8);
-    if constexpr (QT == Dt::BF16) {
-      qb[s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                 ((size_t)t * kHeads + c16) * kQKDim + d0);
-    } else if (!a.q_cast) {
-      q8[s] = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) +
-                                                 ((size_t)t * kHeads + c16) * kQKDim + d0);
-    }
-  }
-  if constexpr (QT == Dt::FP8) {
-    if (a.q_cast) {  // fp8 Q supplied as bf16 (uniform branch)
-      u32x4_t qw[kSteps];
+  for (int q = 0; q < QL; ++q) {
+    const size_t qrow = ((size_t)(pc.t0 + (q < pc.ntok ? q : 0)) * kHeads + c16) * kQKDim;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const int d0 = ((s >> 1) * 4 + g) * 16 + (s & 1) * 8;
-        qw[s] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                 ((size_t)t * kHeads + c16) * kQKDim + d0);
+    for (int s = 0; s < kSteps; ++s) {
+      const int d0 = (KT == Dt::FP8) ? (((s >> 1) * 4 + g) * 16 + (s & 1) * 8) : ((s * 4 + g) * 8);
+      if constexpr (QT == Dt::BF16) {
+        qb[q][s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + d0);
+      } else if (!a.q_cast) {
+        q8[q][s] = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) + qrow + d0);
       }
-      uint32_t posnan = 0;
+    }
+    if constexpr (QT == Dt::FP8) {
+      if (a.q_cast) {  // fp8 Q supplied as bf16 (uniform branch)
+        u32x4_t qw[kSteps];
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) q8[s] = bf16x8_to_e4m3fn(qw[s], posnan);
-      if (__builtin_amdgcn_ballot_w64(posnan != 0u) != 0ull && posnan != 0u) {
-        // rare: a positive NaN in this lane's values; reload them and cast bit by bit
         for (int s = 0; s < kSteps; ++s) {
           const int d0 = ((s >> 1) * 4 + g) * 16 + (s & 1) * 8;
-          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                              ((size_t)t * kHeads + c16) * kQKDim + d0);
-          const uint64_t v = bf16x8_to_e4m3fn_exact(w);
-#pragma unroll
-          for (int s2 = 0; s2 < kSteps; ++s2)
-            if (s2 == s) q8[s2] = v;
+          qw[s] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + d0);
         }
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) q8[q][s] = bf16x8_to_e4m3fn(qw[s]);
       }
     }
   }
 
-  const int T = (ip1 - ip0 + kTileRows - 1) / kTileRows;
+  // tiles up to the furthest row any token of the pass sees
+  int maxlim = 0;
+#pragma unroll
+  for (int q = 0; q < QL; ++q) maxlim = max(maxlim, pc.lim[q]);
+  const int T = (maxlim + kTileRows - 1) / kTileRows;
   const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
 
   // the ring arrives primed: tiles 0..D-1 in flight, indices of D..2D-1 loaded
   auto& dat = ring.dat;
   auto& idxn = ring.next;
-  auto row_index = [&](int tt) {
-    const int pos = ip0 + tt * kTileRows + my_row;
-    return a.kv_indices[pos < ip1 ? pos : ip0];
-  };
-  auto load_tile = [&](u32x4_t(&dst)[L::kChunks], int idx) {
-    const uint8_t* row = kvb + (size_t)idx * L::kRowBytes + g * 16;
+  auto page_index = [&](int tt) { return piece_page(a.kv_indices, pc.ip0, pc.nrows, tt * kTileRows + my_row, sh); };
+  auto load_tile = [&](u32x4_t(&dst)[L::kChunks], int page, int tt) {
+    const int row = page_row(page, pc.nrows, tt * kTileRows + my_row, sh);
+    const uint8_t* src = kvb + (size_t)row * L::kRowBytes + g * 16;
 #pragma unroll
-    for (int j = 0; j < L::kChunks; ++j) dst[j] = *reinterpret_cast<const u32x4_t*>(row + j * 64);
+    for (int j = 0; j < L::kChunks; ++j) dst[j] = *reinterpret_cast<const u32x4_t*>(src + j * 64);
   };
 
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4_t acc[8];
+  float m_run[QL];
+  float l_run[QL];
+  f32x4_t acc[QL][8];
 #pragma unroll
-  for (int jb = 0; jb < 8; ++jb) acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < QL; ++q) {
+    m_run[q] = -INFINITY;
+    l_run[q] = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) acc[q][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // O^T += V^T . P^T over the 64 rows of tile `tt`, this wave's 128 columns.
+  // O^T += V^T . P^T over the 64 rows of tile `tt`, this wave's 128 columns,
+  // for every token of the pass (the V operands are built once).
   // k-step ks covers rows 32ks..32ks+31; slot s of lane group g is row
   // R = 32ks + (s/4)*16 + g*4 + s%4, which is wave 2ks + s/4's row g*4 + s%4.
   // Block jb holds columns 128w + m*8 + jb, m = 0..15; lane c16 feeds m = c16.
@@ -499,14 +550,18 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
     const int buf = tt & 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u32x4_t pp;
-      const u32x2_t p0 = sm.p[buf][2 * ks][lane];
-      const u32x2_t p1 = sm.p[buf][2 * ks + 1][lane];
-      pp[0] = p0[0];
-      pp[1] = p0[1];
-      pp[2] = p1[0];
-      pp[3] = p1[1];
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pp);
+      bf16x8_t pop[QL];
+#pragma unroll
+      for (int q = 0; q < QL; ++q) {
+        u32x4_t pp;
+        const u32x2_t p0 = sm.p[buf][q][2 * ks][lane];
+        const u32x2_t p1 = sm.p[buf][q][2 * ks + 1][lane];
+        pp[0] = p0[0];
+        pp[1] = p0[1];
+        pp[2] = p1[0];
+        pp[3] = p1[1];
+        pop[q] = __builtin_bit_cast(bf16x8_t, pp);
+      }
       if constexpr (KT == Dt::FP8) {
         u32x2_t rv[8];
 #pragma unroll
@@ -531,8 +586,10 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int jb = wd * 4 + u;
-            acc[jb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op[u]), pop, acc[jb], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < QL; ++q)
+              acc[q][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op[u]), pop[q],
+                                                                   acc[q][jb], 0, 0, 0);
           }
         }
       } else {
@@ -549,8 +606,10 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
 #pragma unroll
           for (int pr = 0; pr < 4; ++pr)
             op[pr] = __builtin_amdgcn_perm(rv[2 * pr][jb >> 1], rv[2 * pr + 1][jb >> 1], sel);
-          acc[jb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op), pop, acc[jb], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < QL; ++q)
+            acc[q][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op), pop[q],
+                                                                 acc[q][jb], 0, 0, 0);
         }
       }
     }
@@ -565,82 +624,118 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
   auto step = [&](auto kc, int tt, auto refill) {
     constexpr int k = decltype(kc)::value;
     const int buf = tt & 1;
-    // ---- S^T for this wave's 16 rows (two accumulation chains); V part to LDS
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T for this wave's 16 rows and each token (two accumulation chains); V part to LDS
+    f32x4_t s0[QL], s1[QL];
+#pragma unroll
+    for (int q = 0; q < QL; ++q) {
+      s0[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s1[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     uint8_t* vrow = &sm.v[buf][16 * w + c16][0];
 #pragma unroll
     for (int j = 0; j < L::kChunks; ++j) {
       const u32x4_t kk = dat[k][j];
       if (j < L::kVChunks) *reinterpret_cast<u32x4_t*>(vrow + (j * 4 + g) * 16) = kk;
       if constexpr (KT == Dt::BF16) {
-        if (j & 1)
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk), qb[j], s1, 0, 0, 0);
-        else
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk), qb[j], s0, 0, 0, 0);
+        const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kk);
+#pragma unroll
+        for (int q = 0; q < QL; ++q) {
+          if (j & 1)
+            s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[q][j], s1[q], 0, 0, 0);
+          else
+            s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[q][j], s0[q], 0, 0, 0);
+        }
       } else if constexpr (QT == Dt::BF16) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kk[0], kk[1]), qb[2 * j], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kk[2], kk[3]), qb[2 * j + 1], s1, 0, 0, 0);
+        const bf16x8_t k0 = fp8x8_to_bf16x8(kk[0], kk[1]);
+        const bf16x8_t k1 = fp8x8_to_bf16x8(kk[2], kk[3]);
+#pragma unroll
+        for (int q = 0; q < QL; ++q) {
+          s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[q][2 * j], s0[q], 0, 0, 0);
+          s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[q][2 * j + 1], s1[q], 0, 0, 0);
+        }
       } else {
         const uint64_t k0 = (uint64_t)kk[0] | ((uint64_t)kk[1] << 32);
         const uint64_t k1 = (uint64_t)kk[2] | ((uint64_t)kk[3] << 32);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k0, (long)q8[2 * j], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k1, (long)q8[2 * j + 1], s1, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < QL; ++q) {
+          s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k0, (long)q8[q][2 * j], s0[q], 0, 0, 0);
+          s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k1, (long)q8[q][2 * j + 1], s1[q], 0, 0, 0);
+        }
       }
     }
     // ---- refill this ring slot with tile tt + D, fetch the index of tile tt + 2D.
-    // Issued unconditionally in the steady-state loop (indices past the piece
+    // Issued unconditionally in the steady-state loop (rows past the piece
     // clamp to its first row), so every trip issues the same loads and the
     // compiler's wait counts stay exact: the ring really keeps D tiles in flight.
     if constexpr (decltype(refill)::value) {
-      load_tile(dat[k], idxn[k]);
-      idxn[k] = row_index(tt + 2 * D);
+      load_tile(dat[k], idxn[k], tt + D);
+      idxn[k] = page_index(tt + 2 * D);
     }
     // ---- previous tile's P.V (its weights and V were published before the last barrier)
     if (tt > 0) pv(tt - 1);
-    // ---- scores (log2 domain), masked past the piece end
-    const f32x4_t sc = s0 + s1;
-    float x[4];
-    float mx = -INFINITY;
+    // ---- scores (log2 domain), masked past the rows each token sees
+    float x[QL][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pos = ip0 + tt * kTileRows + 16 * w + g * 4 + i;
-      x[i] = (pos < ip1) ? sc[i] * c_score : -INFINITY;
-      mx = fmaxf(mx, x[i]);
+    for (int q = 0; q < QL; ++q) {
+      const f32x4_t sc = s0[q] + s1[q];
+      float y[4];
+      logit.apply<kGeneral>(sc, y);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pr = tt * kTileRows + 16 * w + g * 4 + i;
+        x[q][i] = (pr < pc.lim[q]) ? y[i] : -INFINITY;
+        mx = fmaxf(mx, x[q][i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (g == 0) sm.mx[buf][w][q][c16] = mx;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (g == 0) sm.mx[buf][w][c16] = mx;
     // ---- speculative weights with the running max known so far
-    auto make_p = [&](u32x2_t& pw) {
-      float pv4[4];
+    u32x2_t pw[QL];
+    auto make_p = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pv4[i] = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
-      pw[0] = pack_bf16x2(pv4[0], pv4[1]);
-      pw[1] = pack_bf16x2(pv4[2], pv4[3]);
-      sm.p[buf][w][lane] = pw;
+      for (int q = 0; q < QL; ++q) {
+        float pv4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv4[i] = (x[q][i] == -INFINITY) ? 0.f : fast_exp2(x[q][i] - m_run[q]);
+        pw[q][0] = pack_bf16x2(pv4[0], pv4[1]);
+        pw[q][1] = pack_bf16x2(pv4[2], pv4[3]);
+        sm.p[buf][q][w][lane] = pw[q];
+      }
     };
-    u32x2_t pw;
-    make_p(pw);
+    make_p();
     __syncthreads();
     // ---- every wave sees the same four maxima, so the decision is workgroup-uniform
-    const float mt =
-        fmaxf(fmaxf(sm.mx[buf][0][c16], sm.mx[buf][1][c16]), fmaxf(sm.mx[buf][2][c16], sm.mx[buf][3][c16]));
-    const bool need = mt > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-      const float m_new = need ? mt : m_run;
-      const float alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
+    float mt[QL];
+    bool need[QL];
+    bool any = false;
 #pragma unroll
-      for (int jb = 0; jb < 8; ++jb) acc[jb] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-      make_p(pw);  // nobody reads tile tt's weights before the next step
+    for (int q = 0; q < QL; ++q) {
+      mt[q] = fmaxf(fmaxf(sm.mx[buf][0][q][c16], sm.mx[buf][1][q][c16]),
+                    fmaxf(sm.mx[buf][2][q][c16], sm.mx[buf][3][q][c16]));
+      need[q] = mt[q] > m_run[q] + kRescaleSlack;
+      any = any || need[q];
+    }
+    if (__builtin_amdgcn_ballot_w64(any) != 0ull) {
+#pragma unroll
+      for (int q = 0; q < QL; ++q) {
+        const float m_new = need[q] ? mt[q] : m_run[q];
+        const float alpha = (m_new == m_run[q]) ? 1.0f : fast_exp2(m_run[q] - m_new);
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) acc[q][jb] *= alpha;
+        l_run[q] *= alpha;
+        m_run[q] = m_new;
+      }
+      make_p();  // nobody reads tile tt's weights before the next step
       __syncthreads();
     }
-    // the row sum uses the same bf16-rounded weights the P.V product sees
+    // the row sums use the same bf16-rounded weights the P.V product sees
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      l_run += __builtin_bit_cast(float, pw[i] << 16) + __builtin_bit_cast(float, pw[i] & 0xFFFF0000u);
+    for (int q = 0; q < QL; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        l_run[q] += __builtin_bit_cast(float, pw[q][i] << 16) + __builtin_bit_cast(float, pw[q][i] & 0xFFFF0000u);
   };
 
   int t0 = 0;
@@ -657,60 +752,86 @@ __device__ void attend_piece(const Args& a, Smem<KT>& sm, int t, int ip0, int ip
   if constexpr (D > 2)
     if (t0 + 2 < T) step(std::integral_constant<int, 2>{}, t0 + 2, std::false_type{});
   static_assert(D <= 4, "ring depth above 4 needs more unrolled steps");
-  pv(T - 1);
+  if (T > 0) pv(T - 1);
 
   // ---- finish: per-head row sums of the 4 waves, then this wave's 128 columns
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (g == 0) sm.lsum[w][c16] = l_tot;
-  __syncthreads();
-  const float Lsum = sm.lsum[0][c16] + sm.lsum[1][c16] + sm.lsum[2][c16] + sm.lsum[3][c16];
-  const float scale = Lsum > 0.f ? out_mul / Lsum : 0.f;
-  // lane (c16, g) holds, for block jb and i < 4, head c16 at column 128w + (4g+i)*8 + jb
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int col = kColsPerWave * w + (4 * g + i) * 8;
-    if (complete) {
-      u32x4_t pk;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(acc[2 * u][i] * scale, acc[2 * u + 1][i] * scale);
-      *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
-    } else {
-      f32x4_t v0, v1;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v0[u] = acc[u][i] * scale;
-        v1[u] = acc[4 + u][i] * scale;
-      }
-      f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)slot * kHeads + c16) * kVDim + col);
-      dst[0] = v0;
-      dst[1] = v1;
-    }
+  for (int q = 0; q < QL; ++q) {
+    float l_tot = l_run[q] + __shfl_xor(l_run[q], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (g == 0) sm.lsum[w][q][c16] = l_tot;
   }
-  if (!complete && w == 0 && g == 0)
-    a.part_lse[slot * kHeads + c16] = Lsum > 0.f ? m_run + fast_log2(Lsum) : -INFINITY;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < QL; ++q) {
+    if (q >= pc.ntok) break;  // uniform
+    const float Lsum = sm.lsum[0][q][c16] + sm.lsum[1][q][c16] + sm.lsum[2][q][c16] + sm.lsum[3][q][c16];
+    const float scale = Lsum > 0.f ? out_mul / Lsum : 0.f;
+    const int t = pc.t0 + q;
+    // lane (c16, g) holds, for block jb and i < 4, head c16 at column 128w + (4g+i)*8 + jb
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = kColsPerWave * w + (4 * g + i) * 8;
+      if (pc.complete) {
+        u32x4_t pk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(acc[q][2 * u][i] * scale, acc[q][2 * u + 1][i] * scale);
+        *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
+      } else {
+        f32x4_t v0, v1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v0[u] = acc[q][u][i] * scale;
+          v1[u] = acc[q][4 + u][i] * scale;
+        }
+        f32x4_t* dst =
+            reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + c16) * kVDim + col);
+        dst[0] = v0;
+        dst[1] = v1;
+      }
+    }
+    if (!pc.complete && w == 0 && g == 0)
+      a.part_lse[(pc.slot + q) * kHeads + c16] = Lsum > 0.f ? m_run[q] + fast_log2(Lsum) : -INFINITY;
+  }
   __syncthreads();  // the shared tile and sums may be reused by the next piece
 }
 
 // ------------------------------------------------------------------ kernels
 
-template <Dt QT, Dt KT, bool kBigBatch>
+// Query tokens and last-page rows of one sequence, packed (tokens << 16) | rows.
+// With one token per sequence at most, qo_e is not read.
+__device__ __forceinline__ int pack_seq_aux(const Args& a, int qo_b, int qo_e, int last_raw, bool paged) {
+  const int ql = a.max_q_len > 1 ? min(max(qo_e - qo_b, 0), a.max_q_len) : 1;
+  const int last = paged ? min(max(last_raw, 1), 1 << a.page_shift) : 1 << a.page_shift;
+  return (ql << 16) | last;
+}
+
+template <Dt QT, Dt KT, bool kBigBatch, int QL, bool kGeneral>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
-  __shared__ Smem<KT> sm;
+  static_assert(kGeneral || QL == 1, "several tokens per walk only in the general form");
+  __shared__ Smem<KT, QL> sm;
+  const int sh = kGeneral ? a.page_shift : 0;
+  const bool paged = a.kv_last_page_len != nullptr && sh > 0;
+  const bool multi = a.max_q_len > 1;  // several tokens per sequence: read qo_indptr[b + 1] too
   // First round trip: the split geometry and the indptr values of up to
   // kScanPerThread sequences per thread (everything the start needs, so no
   // later load has to wait behind the ring's loads: waits count in order).
-  int sv[kScanPerThread][3];
+  // The loads are unconditional (index clamped into the batch, an unpaged
+  // call reads kv_indptr in place of the last-page lengths) and only the raw
+  // values are kept: a branch around a load, or using its value here, would
+  // make each load wait for the previous ones.
+  const int32_t* last_src = paged ? a.kv_last_page_len : a.kv_indptr;
+  int sv[kScanPerThread][5];
 #pragma unroll
   for (int i = 0; i < kScanPerThread; ++i) {
-    const int j = threadIdx.x + i * kThreads;
-    if (j < a.batch) {
-      sv[i][0] = a.kv_indptr[j];
-      sv[i][1] = a.kv_indptr[j + 1];
-      sv[i][2] = a.qo_indptr[j];
-    }
+    const int j = min((int)threadIdx.x + i * kThreads, a.batch - 1);
+    sv[i][0] = a.kv_indptr[j];
+    sv[i][1] = a.kv_indptr[j + 1];
+    sv[i][2] = a.qo_indptr[j];
+    sv[i][3] = a.qo_indptr[j + 1];
+    sv[i][4] = last_src[j];
   }
-  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk);
+  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, sh);
   const int k = blockIdx.x;
   if (k >= geo.n_wg) return;
   const int lo = k * geo.chunk;
@@ -718,22 +839,27 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
 
   const float qs = (QT == Dt::FP8) ? *a.q_scale : 1.0f;
   const float ks = (KT == Dt::FP8) ? *a.kv_scale : 1.0f;
-  const float c_score = a.sm_scale * qs * ks * kLog2e;
+  const float c_nat = a.sm_scale * qs * ks;
+  Logit logit;
+  logit.c_score = c_nat * kLog2e;
+  logit.capped = a.logit_cap > 0.f ? 1 : 0;
+  logit.k1 = logit.capped ? 2.0f * kLog2e * c_nat / a.logit_cap : 0.f;
+  logit.k2 = a.logit_cap * kLog2e;
   const float out_mul = ks;
 
   // The first piece always starts at the share start (the sequence holding
-  // row lo begins at or before it), so its ring can be started now, clamped
-  // to the share, while the scan below finds the sequences.
-  Ring<KT> ring;
-  issue_ring_indices(a.kv_indices, geo.base + lo, geo.base + hi, ring);
-  issue_ring_rows<KT>(a.kv, ring);
+  // position lo begins at or before it), so its ring can be started now,
+  // clamped to the share's pages, while the scan below finds the sequences.
+  Ring<KT, ring_depth<QT, KT, QL>()> ring;
+  issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
+  issue_ring_rows<KT>(a.kv, (hi - lo) << sh, sh, ring);
 
   if (threadIdx.x == 0) {
     sm.bmin = 0x7fffffff;
     sm.bmax = -1;
   }
   __syncthreads();  // bmin / bmax initialised
-  auto scan_one = [&](int j, int ipb, int ipe, int qo) {
+  auto scan_one = [&](int j, int ipb, int ipe, int qo, int aux) {
     const int st = ipb - geo.base;
     const int en = ipe - geo.base;
     if (en > st) {
@@ -745,23 +871,29 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       // an empty sequence belongs to the share holding its position
       int owner = st / geo.chunk;
       if (owner > geo.n_wg - 1) owner = geo.n_wg - 1;
-      if (owner == k) zero_row_by_thread(a.out + (size_t)qo * kHeads * kVDim);
+      if (owner == k)
+        for (int r = 0; r < (aux >> 16); ++r) zero_row_by_thread(a.out + (size_t)(qo + r) * kHeads * kVDim);
     }
   };
 #pragma unroll
   for (int i = 0; i < kScanPerThread; ++i) {
     const int j = threadIdx.x + i * kThreads;
     if (j < a.batch) {
+      const int aux = pack_seq_aux(a, sv[i][2], sv[i][3], sv[i][4], paged);
       if constexpr (!kBigBatch) {
         sm.seq[j][0] = sv[i][0];
         sm.seq[j][1] = sv[i][1];
         sm.seq[j][2] = sv[i][2];
+        sm.seq[j][3] = aux;
       }
-      scan_one(j, sv[i][0], sv[i][1], sv[i][2]);
+      scan_one(j, sv[i][0], sv[i][1], sv[i][2], aux);
     }
   }
-  for (int j = threadIdx.x + kSeqTable; j < a.batch; j += kThreads)
-    scan_one(j, a.kv_indptr[j], a.kv_indptr[j + 1], a.qo_indptr[j]);
+  for (int j = threadIdx.x + kSeqTable; j < a.batch; j += kThreads) {
+    const int qo = a.qo_indptr[j];
+    scan_one(j, a.kv_indptr[j], a.kv_indptr[j + 1], qo,
+             pack_seq_aux(a, qo, multi ? a.qo_indptr[j + 1] : 0, paged ? a.kv_last_page_len[j] : 0, paged));
+  }
   __syncthreads();
   const int bmin = sm.bmin;
   const int bmax = sm.bmax;
@@ -770,29 +902,50 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
     // From the LDS table (batches up to kSeqTable), else from memory.  Two
     // instantiations rather than a runtime select: a select between the two
     // addresses becomes a generic load, whose wait would drain the ring.
-    int ipb, ipe, t;
+    int ipb, ipe, t, aux;
     if constexpr (!kBigBatch) {
       ipb = sm.seq[b][0];
       ipe = sm.seq[b][1];
       t = sm.seq[b][2];
+      aux = sm.seq[b][3];
     } else {
       ipb = a.kv_indptr[b];
       ipe = a.kv_indptr[b + 1];
       t = a.qo_indptr[b];
+      aux = pack_seq_aux(a, t, multi ? a.qo_indptr[b + 1] : 0, paged ? a.kv_last_page_len[b] : 0, paged);
     }
     const int st = ipb - geo.base;
     const int en = ipe - geo.base;
     if (en <= st) continue;
+    const int q_len = aux >> 16;
+    const int n_rows = ((en - st - 1) << sh) + (aux & 0xFFFF);  // the last page may be part-filled
     const int s_lo = max(st, lo);
     const int s_hi = min(en, hi);
     const bool complete = (st >= lo) && (en <= hi);
     const int slot = complete ? -1 : (st <= lo ? 2 * k : 2 * k + 1);
-    if (b != bmin) {
-      issue_ring_indices(a.kv_indices, s_lo + geo.base, s_hi + geo.base, ring);
-      issue_ring_rows<KT>(a.kv, ring);
+    const int r0 = (s_lo - st) << sh;  // the piece's first row within the sequence
+    const int nrows = min((s_hi - st) << sh, n_rows) - r0;
+    for (int tau0 = 0; tau0 < q_len; tau0 += QL) {
+      Piece<QL> pc;
+      pc.ip0 = s_lo + geo.base;
+      pc.nrows = nrows;
+      pc.t0 = t + tau0;
+      pc.ntok = min(QL, q_len - tau0);
+#pragma unroll
+      for (int q = 0; q < QL; ++q) {
+        // causal: token tau of q_len sees the sequence's first n_rows - q_len + 1 + tau rows
+        const int vis = a.causal ? n_rows - q_len + 1 + tau0 + q : n_rows;
+        pc.lim[q] = (q < pc.ntok) ? min(nrows, vis - r0) : 0;
+      }
+      pc.slot = complete ? -1 : slot * a.max_q_len + tau0;
+      pc.complete = complete;
+      if (b != bmin || tau0 != 0) {
+        issue_ring_indices(a.kv_indices, pc.ip0, nrows, sh, ring);
+        issue_ring_rows<KT>(a.kv, nrows, sh, ring);
+      }
+      attend_piece<QT, KT, QL, kGeneral>(a, sm, pc, logit, out_mul, ring);
     }
-    attend_piece<QT, KT>(a, sm, t, s_lo + geo.base, s_hi + geo.base, complete, slot, c_score, out_mul, ring);
-    if (!complete && a.fused) {
+    if (!complete && a.fused && q_len > 0) {
       __threadfence();
       __syncthreads();
       if (threadIdx.x == 0) sm.arrive = atomicAdd(&a.counters[b], 1);
@@ -801,12 +954,15 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       if (sm.arrive == S - 1) {
         __threadfence();
         const int chunk = geo.chunk;
+        const int qmax = a.max_q_len;
         const int w = threadIdx.x >> 6;
-        for (int hh = 0; hh < kHeads / kWaves; ++hh) {
-          const int h = w * (kHeads / kWaves) + hh;
-          merge_head_wave(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f, h,
-                          a.out + ((size_t)t * kHeads + h) * kVDim);
-        }
+        for (int tau = 0; tau < q_len; ++tau)
+          for (int hh = 0; hh < kHeads / kWaves; ++hh) {
+            const int h = w * (kHeads / kWaves) + hh;
+            merge_head_wave(
+                a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i) * qmax + tau; }, 1.0f, h,
+                a.out + ((size_t)(t + tau) * kHeads + h) * kVDim);
+          }
         if (threadIdx.x == 0) atomicExch(&a.counters[b], 0);
       }
       __syncthreads();
@@ -814,20 +970,28 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   }
 }
 
-// Separate merge launch: one wave per (sequence, head); sequences that were
-// not split were finished by the attention kernel and are skipped.
+// Separate merge launch: one wave per (sequence, head, token); sequences that
+// were not split were finished by the attention kernel and are skipped.
 __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int b = blockIdx.x;
   const int h = blockIdx.y;
-  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk);
+  const int tau = blockIdx.z;
+  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, a.page_shift);
   const int st = a.kv_indptr[b] - geo.base;
   const int en = a.kv_indptr[b + 1] - geo.base;
   if (en <= st) return;
+  const int qo = a.qo_indptr[b];
+  if (a.max_q_len > 1) {
+    const int q_len = min(max(a.qo_indptr[b + 1] - qo, 0), a.max_q_len);
+    if (tau >= q_len) return;
+  }
   const int S = piece_count(st, en, geo.chunk);
   if (S <= 1) return;
   const int chunk = geo.chunk;
-  merge_head_wave(a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i); }, 1.0f, h,
-                  a.out + ((size_t)a.qo_indptr[b] * kHeads + h) * kVDim);
+  const int qmax = a.max_q_len;
+  merge_head_wave(
+      a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i) * qmax + tau; }, 1.0f, h,
+      a.out + ((size_t)(qo + tau) * kHeads + h) * kVDim);
 }
 
 // Merge of caller-provided partials (natural-log lse), one wave per (sequence, head).
@@ -857,10 +1021,7 @@ __global__ void mla_quantize_q_kernel(const uint16_t* __restrict__ src, uint8_t*
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n; i += stride) {
     if (i + 8 <= n && ((reinterpret_cast<uintptr_t>(src + i) & 15u) == 0) && ((reinterpret_cast<uintptr_t>(dst + i) & 7u) == 0)) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + i);
-      uint32_t posnan = 0;
-      uint64_t o = bf16x8_to_e4m3fn(v, posnan);
-      if (posnan) o = bf16x8_to_e4m3fn_exact(v);
-      *reinterpret_cast<uint64_t*>(dst + i) = o;
+      *reinterpret_cast<uint64_t*>(dst + i) = bf16x8_to_e4m3fn(v);
     } else {
       for (int64_t j = i; j < n && j < i + 8; ++j) dst[j] = (uint8_t)bf16_to_e4m3fn(src[j]);
     }

@@ -5,22 +5,27 @@ attention arithmetic.  Everything is generated on the CPU with
 ``torch.Generator`` so the float64 oracle and the GPU read the very same bytes.
 
 Recipe (the workload shapes of the kernelindex amd-mixed-mla submissions:
-16 heads x 576 over one 576-wide latent KV head, page size 1; the harness's
-own generator is not on the pages, so these distributions stand in for it):
+16 heads x 576 over one 576-wide latent KV head, page size 1 for the decode
+configurations; the harness's own generator is not on the pages, so these
+distributions stand in for it):
 
-* Q: ``randn`` float32 -> bf16, shape [batch, 16, 576] (one query token per
-  sequence).  fp8 Q is *not* made here: casting Q is step a0 of the path and
-  is done by the library (or by the oracle's own encoder) from these bf16 bits.
+* Q: ``randn`` float32 -> bf16, shape [total_q, 16, 576] (one query token per
+  sequence unless ``q_lens`` gives more).  fp8 Q is *not* made here: casting
+  Q is step a0 of the path and is done by the library (or by the oracle's own
+  encoder) from these bf16 bits.
 * bf16 KV: ``randn`` float32 -> bf16, shape [rows, 576].
 * fp8 KV: ``randn`` float32, per-tensor scale ``amax(|kv|) / 448`` in float32,
   then ``(kv / scale).to(float8_e4m3fn)`` (torch's cast); the scale is returned
   next to the codes, as the pages receive ``(kv_fp8, kv_scale)``.
 * lengths: a fixed length per sequence, or ``randint(1, max_len + 1)`` per
   sequence for the ragged case.
-* ``kv_indptr`` = exclusive cumulative sum of the lengths; ``qo_indptr`` =
-  ``arange(batch + 1)``.
+* pages of ``page_size`` rows: sequence b of L rows takes ceil(L / page_size)
+  pages, the last one holding ``kv_last_page_len[b]`` rows (the unused slots
+  keep their random values, so a kernel that reads them is caught).
+* ``kv_indptr`` = exclusive cumulative sum of the pages per sequence;
+  ``qo_indptr`` = exclusive cumulative sum of the query tokens per sequence.
 * ``kv_indices``: ``arange`` (contiguous pool) or a seeded ``randperm`` of the
-  pool rows (ragged, paged case).
+  pool pages (ragged, paged case).
 """
 
 from __future__ import annotations
@@ -47,6 +52,8 @@ class CaseSpec:
     permuted: bool = False  # kv_indices = randperm(pool) instead of arange
     extra_pool_rows: int = 0  # pool rows not referenced by any sequence (permuted pools)
     seed: int = 0  # base seed; Q/KV/lengths/permutation use seed+1..seed+4
+    page_size: int = 1  # rows per page
+    q_lens: Optional[Sequence[int]] = None  # query tokens per sequence (None: one each)
 
     @property
     def name(self) -> str:
@@ -57,17 +64,23 @@ class CaseSpec:
 @dataclasses.dataclass
 class Case:
     spec: CaseSpec
-    q_bf16: torch.Tensor  # [batch, 16, 576] bf16
-    kv: torch.Tensor  # [rows, 576] bf16 or float8_e4m3fn
+    q_bf16: torch.Tensor  # [total_q, 16, 576] bf16
+    kv: torch.Tensor  # [pool_pages * page_size, 576] bf16 or float8_e4m3fn
     kv_scale: Optional[torch.Tensor]  # [1] float32 for fp8 KV, else None
     qo_indptr: torch.Tensor  # [batch + 1] int32
-    kv_indptr: torch.Tensor  # [batch + 1] int32
-    kv_indices: torch.Tensor  # [sum(lengths)] int32
-    lengths: torch.Tensor  # [batch] int64
+    kv_indptr: torch.Tensor  # [batch + 1] int32, in pages
+    kv_indices: torch.Tensor  # [total pages] int32
+    lengths: torch.Tensor  # [batch] int64, rows per sequence
+    kv_last_page_len: Optional[torch.Tensor] = None  # [batch] int32, rows in each last page
 
     @property
     def total_kv(self) -> int:
-        return int(self.kv_indptr[-1])
+        """KV rows over all sequences."""
+        return int(self.lengths.sum())
+
+    @property
+    def total_q(self) -> int:
+        return int(self.qo_indptr[-1])
 
     def q_bits(self) -> torch.Tensor:
         """bf16 Q as raw 16-bit patterns (int16 storage)."""
@@ -95,10 +108,17 @@ def make_case(spec: CaseSpec) -> Case:
         lengths = torch.randint(1, spec.ragged_max + 1, (B,), generator=_gen(spec.seed + 3), dtype=torch.int64)
     else:
         lengths = torch.full((B,), spec.kv_len, dtype=torch.int64)
-    total = int(lengths.sum())
-    rows = total + spec.extra_pool_rows
+    ps = spec.page_size
+    pages = (lengths + ps - 1) // ps
+    total_pages = int(pages.sum())
+    pool_pages = total_pages + (spec.extra_pool_rows + ps - 1) // ps
+    rows = pool_pages * ps
+    q_lens = torch.ones(B, dtype=torch.int64) if spec.q_lens is None else torch.tensor(list(spec.q_lens))
+    assert q_lens.numel() == B
+    total_q = int(q_lens.sum())
 
-    q = torch.randn((B, NUM_HEADS, QK_DIM), generator=_gen(spec.seed + 1), dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((total_q, NUM_HEADS, QK_DIM), generator=_gen(spec.seed + 1), dtype=torch.float32).to(
+        torch.bfloat16)
 
     kv32 = torch.randn((rows, QK_DIM), generator=_gen(spec.seed + 2), dtype=torch.float32)
     if spec.kv_dtype == "bf16":
@@ -114,20 +134,24 @@ def make_case(spec: CaseSpec) -> Case:
     del kv32
 
     kv_indptr = torch.zeros(B + 1, dtype=torch.int64)
-    kv_indptr[1:] = torch.cumsum(lengths, 0)
+    kv_indptr[1:] = torch.cumsum(pages, 0)
+    qo_indptr = torch.zeros(B + 1, dtype=torch.int64)
+    qo_indptr[1:] = torch.cumsum(q_lens, 0)
     if spec.permuted:
-        kv_indices = torch.randperm(rows, generator=_gen(spec.seed + 4))[:total]
+        kv_indices = torch.randperm(pool_pages, generator=_gen(spec.seed + 4))[:total_pages]
     else:
-        kv_indices = torch.arange(total, dtype=torch.int64)
+        kv_indices = torch.arange(total_pages, dtype=torch.int64)
+    last = torch.where(pages > 0, lengths - (pages - 1) * ps, torch.full_like(lengths, ps))
     return Case(
         spec=spec,
         q_bf16=q,
         kv=kv,
         kv_scale=kv_scale,
-        qo_indptr=torch.arange(B + 1, dtype=torch.int32),
+        qo_indptr=qo_indptr.to(torch.int32),
         kv_indptr=kv_indptr.to(torch.int32),
         kv_indices=kv_indices.to(torch.int32),
         lengths=lengths,
+        kv_last_page_len=last.to(torch.int32),
     )
 
 

@@ -33,6 +33,10 @@ class DevCase:
         self.qo_indptr = case.qo_indptr.to(dev)
         self.kv_indptr = case.kv_indptr.to(dev)
         self.kv_indices = case.kv_indices.to(dev)
+        self.kv_last_page_len = case.kv_last_page_len.to(dev) if case.kv_last_page_len is not None else None
+        self.page_size = case.spec.page_size
+        self.total_q = case.total_q
+        self.max_q_len = int((case.qo_indptr[1:] - case.qo_indptr[:-1]).max())
         self.q_dtype = case.spec.q_dtype
         self.kv_dtype = case.spec.kv_dtype
         if self.q_dtype == "fp8":
@@ -48,23 +52,32 @@ class DevCase:
         return self.case.spec.batch
 
     def decoder(self, **kw) -> binding.Decoder:
+        kw.setdefault("page_size", self.page_size)
+        kw.setdefault("max_q_len", self.max_q_len if self.max_q_len > 1 else 0)
+        kw.setdefault("total_q", self.total_q)
         return binding.Decoder(self.batch, self.q_dtype, self.kv_dtype, self.dev, **kw)
 
     def run(self, dec: binding.Decoder | None = None, out: torch.Tensor | None = None, q_cast: bool = False,
-            **kw) -> torch.Tensor:
-        """One decode step; with q_cast the fp8 Q is cast inside the attention kernel from the bf16 Q."""
+            causal: bool = False, paged: bool | None = None, **kw) -> torch.Tensor:
+        """One decode step; with q_cast the fp8 Q is cast inside the attention kernel from the bf16 Q.
+
+        Pages of more than one row go through mla_decode_run_paged with the case's last-page lengths
+        (``paged`` forces either entry point)."""
         if q_cast:
             kw["flags"] = kw.get("flags", 0) | binding.MLA_FLAG_FUSED_Q_CAST
+        if causal:
+            kw["flags"] = kw.get("flags", 0) | binding.MLA_FLAG_CAUSAL
         dec = dec or self.decoder(**kw)
         if out is None:
-            out = torch.full((self.batch, 16, 512), float("nan"), dtype=torch.bfloat16, device=self.dev)
+            out = torch.full((self.total_q, 16, 512), float("nan"), dtype=torch.bfloat16, device=self.dev)
         q = self.q_bf16 if q_cast else self.q
+        use_paged = self.page_size > 1 if paged is None else paged
         dec.run(q, self.kv, self.qo_indptr, self.kv_indptr, self.kv_indices, self.q_scale, self.kv_scale,
-                oracle.SM_SCALE, out)
+                oracle.SM_SCALE, out, kv_last_page_len=self.kv_last_page_len if use_paged else None)
         return out
 
 
-def oracle_ref(case: synth.Case, sequences=None) -> np.ndarray:
+def oracle_ref(case: synth.Case, sequences=None, causal: bool = False, logit_cap: float = 0.0) -> np.ndarray:
     """float64 oracle on the same host bytes (fp8 Q from the oracle's own encoder)."""
     q_bits = case.q_bits().numpy()
     if case.spec.q_dtype == "fp8":
@@ -75,7 +88,9 @@ def oracle_ref(case: synth.Case, sequences=None) -> np.ndarray:
     kv_scale = float(case.kv_scale[0]) if case.kv_scale is not None else None
     return oracle.mla_decode(q_bits, case.kv_bits().numpy(), case.qo_indptr.numpy(), case.kv_indptr.numpy(),
                              case.kv_indices.numpy(), q_dtype=case.spec.q_dtype, kv_dtype=case.spec.kv_dtype,
-                             q_scale=q_scale, kv_scale=kv_scale, sequences=sequences)
+                             q_scale=q_scale, kv_scale=kv_scale, sequences=sequences,
+                             page_size=case.spec.page_size, kv_last_page_len=case.kv_last_page_len.numpy(),
+                             causal=causal, logit_cap=logit_cap)
 
 
 def to64(t: torch.Tensor) -> np.ndarray:

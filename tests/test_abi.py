@@ -23,8 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["mla_decode_workspace_size", "mla_decode_plan", "mla_decode_run", "mla_decode_quantize_q",
-              "mla_decode_reduce", "mla_status_string", "mla_decode_abi_version"]:
+    for n in ["mla_decode_workspace_size", "mla_decode_plan", "mla_decode_run", "mla_decode_run_paged",
+              "mla_decode_quantize_q", "mla_decode_reduce", "mla_status_string", "mla_decode_abi_version"]:
         assert n in names
 
 
@@ -35,13 +35,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # 12 int32 fields; the plan carries params + pointer + size + 2 int32 + 3 offsets
-    assert ctypes.sizeof(B.MlaDecodeParams) == 48
-    assert ctypes.sizeof(B.MlaDecodePlan) == 48 + 8 + 8 + 8 + 24
+    # 13 int32 fields and one float; the plan carries params + pointer + size + 2 int32 + 3 offsets
+    assert ctypes.sizeof(B.MlaDecodeParams) == 56
+    assert ctypes.sizeof(B.MlaDecodePlan) == 56 + 8 + 8 + 8 + 24
 
 
 def test_abi_version_and_status_strings():
-    assert B.mla_decode_abi_version() == 1
+    assert B.mla_decode_abi_version() == 2
     for code in range(5):
         s = B.mla_status_string(code)
         assert s.startswith("MLA_")
@@ -60,6 +60,9 @@ def test_workspace_size_is_host_arithmetic():
     # counters (64 int32, padded to 256 B) + partial O (2*256*16*512 fp32) + partial lse (2*256*16 fp32)
     assert n == 256 + 2 * 256 * 16 * 512 * 4 + 2 * 256 * 16 * 4
     assert B.mla_decode_workspace_size(_params(batch=1000, num_units=4)) == 4096 + 2 * 4 * 16 * 512 * 4 + 512
+    # with several query tokens every partial slot has a row per token
+    assert B.mla_decode_workspace_size(_params(batch=64, total_q=128, num_units=256, max_q_len=2)) == \
+        256 + 2 * 2 * 256 * 16 * 512 * 4 + 2 * 2 * 256 * 16 * 4
 
 
 @pytest.mark.parametrize(
@@ -77,14 +80,24 @@ def test_workspace_size_is_host_arithmetic():
         (dict(num_kv_heads=2), B.MLA_ERR_UNSUPPORTED),
         (dict(qk_dim=512, v_dim=512), B.MLA_ERR_UNSUPPORTED),
         (dict(v_dim=128), B.MLA_ERR_UNSUPPORTED),
-        (dict(page_size=16), B.MLA_ERR_UNSUPPORTED),
-        (dict(total_q=8), B.MLA_ERR_UNSUPPORTED),
+        (dict(page_size=0), B.MLA_ERR_INVALID_ARG),
+        (dict(page_size=12), B.MLA_ERR_UNSUPPORTED),
+        (dict(page_size=2048), B.MLA_ERR_UNSUPPORTED),
+        (dict(total_q=8), B.MLA_ERR_INVALID_ARG),  # more query rows than batch * max_q_len
+        (dict(total_q=3), B.MLA_ERR_INVALID_ARG),  # fewer than one per sequence
+        (dict(total_q=65, max_q_len=16), B.MLA_ERR_INVALID_ARG),
+        (dict(max_q_len=-1), B.MLA_ERR_INVALID_ARG),
+        (dict(max_q_len=17, total_q=8), B.MLA_ERR_UNSUPPORTED),
+        (dict(logit_cap=-1.0), B.MLA_ERR_INVALID_ARG),
+        (dict(logit_cap=float("nan")), B.MLA_ERR_INVALID_ARG),
+        (dict(logit_cap=float("inf")), B.MLA_ERR_INVALID_ARG),
         (dict(q_dtype="fp8", kv_dtype="bf16"), B.MLA_ERR_UNSUPPORTED),
         (dict(flags=B.MLA_FLAG_FUSED_Q_CAST), B.MLA_ERR_INVALID_ARG),  # needs fp8 q_dtype
-        (dict(flags=4), B.MLA_ERR_INVALID_ARG),
+        (dict(flags=16), B.MLA_ERR_INVALID_ARG),
     ],
 )
 def test_plan_rejects_bad_params_before_any_hip_call(kw, code):
+    """Every rejection happens on the host: no device is needed to see it."""
     p = _params(**kw)
     plan = B.MlaDecodePlan()
     got = B.lib().mla_decode_plan(ctypes.byref(p), 4096, 1 << 30, None, ctypes.byref(plan))
@@ -170,3 +183,10 @@ def test_binding_has_no_cpu_fallback():
     # the product path refuses host tensors instead of computing on the CPU
     with pytest.raises(ValueError):
         B._ptr(torch.zeros(4))
+
+
+@pytest.mark.parametrize("kw", [dict(page_size=16), dict(page_size=1024), dict(max_q_len=4, total_q=13),
+                                dict(flags=B.MLA_FLAG_CAUSAL, max_q_len=2, total_q=8), dict(logit_cap=30.0)])
+def test_widened_params_pass_host_validation(kw):
+    # accepted shapes get a workspace size with explicit units (no device query needed)
+    assert B.mla_decode_workspace_size(_params(**kw)) > 0

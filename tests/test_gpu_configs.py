@@ -7,6 +7,8 @@ output: it is finite, and each element lies within the range of its
 sequence's V column (the output is a convex combination of V rows).
 """
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -61,7 +63,7 @@ def test_full_config(gpu, name):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out.float()).all())
     assert convex_bound_ok(dc, out)
-    seqs = sample_sequences(case, seed=hash(name) % 1000)
+    seqs = sample_sequences(case, seed=zlib.crc32(name.encode()) % 1000)
     with Timer(f"oracle on {len(seqs)} sequences"):
         ref = oracle_ref(case, sequences=seqs)
     got = to64(out)
