@@ -189,6 +189,23 @@ mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, co
 mla_status mla_decode_quantize_q(const void* q_bf16, void* q_fp8, int64_t n, hipStream_t stream);
 
 /*
+ * Step a0 with a per-tensor scale (the amax pass that submission 689529's
+ * docstring names as the step it skips):
+ *   amax    = max |q| over the finite values of q_bf16,
+ *   q_scale = amax / 448 in float32 (1 when amax is 0),
+ *   q_fp8   = e4m3fn(q / q_scale), the division in float32 (correctly
+ *             rounded), round-to-nearest-even, no saturation; +-inf and
+ *             NaN give the NaN code with the input's sign.
+ * q_scale (one float32 in device memory) is then the q_scale argument of
+ * mla_decode_run.  scratch: device memory of at least
+ * MLA_QUANT_DYNAMIC_SCRATCH_BYTES, 4-byte aligned, overwritten.  Two
+ * launches on `stream`; n may be 0 (q_scale becomes 1).
+ */
+#define MLA_QUANT_DYNAMIC_SCRATCH_BYTES 1024
+mla_status mla_decode_quantize_q_dynamic(const void* q_bf16, void* q_fp8, float* q_scale, void* scratch,
+                                         size_t scratch_bytes, int64_t n, hipStream_t stream);
+
+/*
  * Merge split partials produced elsewhere (e.g. KV shards on other devices):
  * for every sequence b and head h, with p in [part_indptr[b], part_indptr[b+1]),
  *   w_p = exp(lse[p,h] - max_p lse[p,h]),  out[b,h,:] = sum_p w_p o[p,h,:] / sum_p w_p

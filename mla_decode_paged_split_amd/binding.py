@@ -36,6 +36,8 @@ __all__ = [
     "mla_decode_run",
     "mla_decode_run_paged",
     "mla_decode_quantize_q",
+    "mla_decode_quantize_q_dynamic",
+    "MLA_QUANT_DYNAMIC_SCRATCH_BYTES",
     "mla_decode_reduce",
     "make_params",
     "Decoder",
@@ -51,6 +53,7 @@ MLA_DTYPE_FP8_E4M3FN = 1
 MLA_FLAG_FUSED_MERGE = 1
 MLA_FLAG_FUSED_Q_CAST = 2
 MLA_FLAG_CAUSAL = 4
+MLA_QUANT_DYNAMIC_SCRATCH_BYTES = 1024
 
 _DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3FN}
 
@@ -118,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run_paged.restype = ctypes.c_int
         L.mla_decode_quantize_q.argtypes = [vp, vp, i64, vp]
         L.mla_decode_quantize_q.restype = ctypes.c_int
+        L.mla_decode_quantize_q_dynamic.argtypes = [vp, vp, vp, vp, sz, i64, vp]
+        L.mla_decode_quantize_q_dynamic.restype = ctypes.c_int
         L.mla_decode_reduce.argtypes = [vp, vp, vp, i32, vp, vp]
         L.mla_decode_reduce.restype = ctypes.c_int
         _LIB = L
@@ -222,6 +227,18 @@ def mla_decode_quantize_q(q_bf16: torch.Tensor, q_fp8: torch.Tensor, stream=None
         raise ValueError("expected bf16 input and a 1-byte output of the same size")
     code = lib().mla_decode_quantize_q(_ptr(q_bf16), _ptr(q_fp8), q_bf16.numel(), _stream(stream))
     _check(code, "mla_decode_quantize_q")
+
+
+def mla_decode_quantize_q_dynamic(q_bf16: torch.Tensor, q_fp8: torch.Tensor, q_scale: torch.Tensor,
+                                  scratch: torch.Tensor, stream=None) -> None:
+    if q_bf16.dtype != torch.bfloat16 or q_fp8.element_size() != 1 or q_fp8.numel() != q_bf16.numel():
+        raise ValueError("expected bf16 input and a 1-byte output of the same size")
+    if q_scale.dtype != torch.float32 or q_scale.numel() < 1:
+        raise ValueError("q_scale must be a float32 tensor of at least one element")
+    code = lib().mla_decode_quantize_q_dynamic(_ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale), _ptr(scratch),
+                                               scratch.numel() * scratch.element_size(), q_bf16.numel(),
+                                               _stream(stream))
+    _check(code, "mla_decode_quantize_q_dynamic")
 
 
 def mla_decode_reduce(part_o: torch.Tensor, part_lse: torch.Tensor, part_indptr: torch.Tensor, out: torch.Tensor,

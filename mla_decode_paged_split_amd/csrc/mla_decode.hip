@@ -261,6 +261,32 @@ mla_status mla_decode_quantize_q(const void* q_bf16, void* q_fp8, int64_t n, hip
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+mla_status mla_decode_quantize_q_dynamic(const void* q_bf16, void* q_fp8, float* q_scale, void* scratch,
+                                         size_t scratch_bytes, int64_t n, hipStream_t stream) {
+  if (n < 0 || q_scale == nullptr) return MLA_ERR_INVALID_ARG;
+  if (scratch == nullptr || scratch_bytes < MLA_QUANT_DYNAMIC_SCRATCH_BYTES ||
+      (reinterpret_cast<uintptr_t>(scratch) & 3u) != 0)
+    return MLA_ERR_WORKSPACE;
+  if (n > 0 && (q_bf16 == nullptr || q_fp8 == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (n > 0) {
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(q_bf16), s1 = s0 + (uintptr_t)n * 2;
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(q_fp8), d1 = d0 + (uintptr_t)n;
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(scratch), w1 = w0 + MLA_QUANT_DYNAMIC_SCRATCH_BYTES;
+    if ((s0 < d1 && d0 < s1) || (w0 < d1 && d0 < w1) || (w0 < s1 && s0 < w1)) return MLA_ERR_INVALID_ARG;
+  }
+  int64_t parts = (n + 256 * 8 - 1) / (256 * 8);
+  parts = parts < 1 ? 1 : (parts > 256 ? 256 : parts);
+  int64_t blocks = (n + 256 * 8 - 1) / (256 * 8);
+  blocks = blocks < 1 ? 1 : (blocks > 65535 ? 65535 : blocks);
+  uint32_t* partial = static_cast<uint32_t*>(scratch);
+  const uint16_t* src = static_cast<const uint16_t*>(q_bf16);
+  hipLaunchKernelGGL(mla::mla_q_amax_kernel, dim3((unsigned)parts), dim3(256), 0, stream, src, n, partial);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  hipLaunchKernelGGL(mla::mla_q_cast_scaled_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src,
+                     static_cast<uint8_t*>(q_fp8), n, partial, (int)parts, q_scale);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const int32_t* part_indptr, int32_t batch,
                              void* out, hipStream_t stream) {
   if (batch < 1 || part_indptr == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;

@@ -1028,4 +1028,100 @@ __global__ void mla_quantize_q_kernel(const uint16_t* __restrict__ src, uint8_t*
   }
 }
 
+// ------------------------------------------- step a0, amax-scaled variant
+
+// float32 -> e4m3fn, round to nearest even, non-saturating (the conventions
+// of bf16_to_e4m3fn), on the bit fields.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(uint32_t x) {
+  const uint32_t sign = (x >> 24) & 0x80u;
+  const int e = (int)((x >> 23) & 0xFFu);
+  const uint32_t m = x & 0x7FFFFFu;
+  if (e == 0xFF) return sign | 0x7Fu;
+  int E = e - 127 + 7;  // e4m3 biased exponent
+  if (E >= 1) {
+    uint32_t m3 = m >> 20;
+    const uint32_t rem = m & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) {
+      m3 = 0;
+      ++E;
+    }
+    if (E > 15 || (E == 15 && m3 == 7u)) return sign | 0x7Fu;
+    return sign | ((uint32_t)E << 3) | m3;
+  }
+  // below 2^-6: units of 2^-9; the 24-bit significand is scaled by 2^(e - 141)
+  const int shift = 141 - e;
+  if (e == 0 || shift > 24) return sign;  // below 2^-10 rounds to zero (2^-10 itself is a tie to even 0)
+  const uint32_t sig = 0x800000u | m;
+  uint32_t n = sig >> shift;
+  const uint32_t rem = sig & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (n & 1u))) ++n;
+  return sign | n;  // n == 8 is the smallest normal, encoded the same way
+}
+
+// |x| of a finite bf16 as ordered bits (0 for +-inf and NaN, which do not enter the amax).
+__device__ __forceinline__ uint32_t finite_abs_bits(uint32_t h) {
+  const uint32_t a = h & 0x7FFFu;
+  return a < 0x7F80u ? a : 0u;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = max(max(red[0], red[1]), max(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+// Pass 1: each workgroup's amax over its grid-stride share, as ordered bits.
+__global__ __launch_bounds__(256) void mla_q_amax_kernel(const uint16_t* __restrict__ src, int64_t n,
+                                                         uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+    const int64_t groups = n / 8;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < groups; i += stride) {
+      const u32x4_t v = reinterpret_cast<const u32x4_t*>(src)[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = max(m, max(finite_abs_bits(v[k] & 0xFFFFu), finite_abs_bits(v[k] >> 16)));
+    }
+    for (int64_t i = groups * 8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+      m = max(m, finite_abs_bits(src[i]));
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) m = max(m, finite_abs_bits(src[i]));
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// Pass 2: every workgroup reduces the nparts (<= 256) partial maxima,
+// q_scale = amax / 448 in float32 (1 when amax is 0), and casts its share of
+// q / q_scale (float32 division, correctly rounded) to e4m3fn; +-inf and NaN
+// inputs give the NaN code with their sign.  Workgroup 0 stores q_scale.
+__global__ __launch_bounds__(256) void mla_q_cast_scaled_kernel(const uint16_t* __restrict__ src,
+                                                                uint8_t* __restrict__ dst, int64_t n,
+                                                                const uint32_t* __restrict__ partial, int nparts,
+                                                                float* __restrict__ q_scale) {
+  __shared__ uint32_t red[4];
+  const uint32_t m = block_max_u32(threadIdx.x < (unsigned)nparts ? partial[threadIdx.x] : 0u, red);
+  const float amax = __builtin_bit_cast(float, m << 16);
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *q_scale = scale;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const uint32_t h = src[i];
+    uint32_t code;
+    if ((h & 0x7FFFu) >= 0x7F80u) {
+      code = ((h >> 8) & 0x80u) | 0x7Fu;
+    } else {
+      const float y = __builtin_bit_cast(float, h << 16) / scale;
+      code = f32_to_e4m3fn(__builtin_bit_cast(uint32_t, y));
+    }
+    dst[i] = (uint8_t)code;
+  }
+}
+
 }  // namespace mla

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["mla_decode_workspace_size", "mla_decode_plan", "mla_decode_run", "mla_decode_run_paged",
-              "mla_decode_quantize_q", "mla_decode_reduce", "mla_status_string", "mla_decode_abi_version"]:
+              "mla_decode_quantize_q", "mla_decode_quantize_q_dynamic", "mla_decode_reduce", "mla_status_string",
+              "mla_decode_abi_version"]:
         assert n in names
 
 
@@ -166,6 +167,15 @@ def test_quantize_and_reduce_argument_checks():
     assert L.mla_decode_quantize_q(None, 4096, 10, None) == B.MLA_ERR_INVALID_ARG
     # overlapping source and destination
     assert L.mla_decode_quantize_q(4096, 4100, 10, None) == B.MLA_ERR_INVALID_ARG
+    D = L.mla_decode_quantize_q_dynamic
+    assert D(4096, 1 << 20, 8192, 1 << 24, 1024, -1, None) == B.MLA_ERR_INVALID_ARG  # negative size
+    assert D(4096, 1 << 20, None, 1 << 24, 1024, 10, None) == B.MLA_ERR_INVALID_ARG  # no q_scale
+    assert D(4096, 1 << 20, 8192, None, 1024, 10, None) == B.MLA_ERR_WORKSPACE  # no scratch
+    assert D(4096, 1 << 20, 8192, 1 << 24, 1023, 10, None) == B.MLA_ERR_WORKSPACE  # scratch too small
+    assert D(4096, 1 << 20, 8192, (1 << 24) + 2, 1024, 10, None) == B.MLA_ERR_WORKSPACE  # misaligned
+    assert D(None, 1 << 20, 8192, 1 << 24, 1024, 10, None) == B.MLA_ERR_INVALID_ARG
+    assert D(4096, 4100, 8192, 1 << 24, 1024, 10, None) == B.MLA_ERR_INVALID_ARG  # q overlaps its output
+    assert D(4096, 1 << 20, 8192, (1 << 20) + 4, 1024, 10, None) == B.MLA_ERR_INVALID_ARG  # scratch overlaps
     assert L.mla_decode_reduce(4096, 4096, 4096, 0, 4096, None) == B.MLA_ERR_INVALID_ARG
     assert L.mla_decode_reduce(None, 4096, 4096, 2, 4096, None) == B.MLA_ERR_INVALID_ARG
     assert L.mla_decode_reduce(4096, 4096, None, 2, 4096, None) == B.MLA_ERR_INVALID_ARG

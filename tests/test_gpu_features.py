@@ -130,3 +130,77 @@ def test_everything_combined(gpu):
         assert_parity(ref, to64(out), f"combined u{units} f{flags}")
     fused = dc.run(num_units=64, min_chunk=32, causal=True, logit_cap=5.0, q_cast=True)
     assert_parity(ref, to64(fused), "combined fused cast")
+
+
+# ------------------------------------------------------- amax-scaled Q cast
+
+import oracle  # noqa: E402
+
+
+def _dyn_cast(gpu, bits_np):
+    src = torch.from_numpy(bits_np.astype(np.int16)).view(torch.bfloat16).to(gpu)
+    dst = torch.empty(src.numel(), dtype=torch.uint8, device=gpu)
+    scale = torch.full((1,), -1.0, dtype=torch.float32, device=gpu)
+    scratch = torch.empty(binding.MLA_QUANT_DYNAMIC_SCRATCH_BYTES, dtype=torch.uint8, device=gpu)
+    binding.mla_decode_quantize_q_dynamic(src.reshape(-1), dst, scale, scratch)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy(), float(scale.cpu()[0])
+
+
+@pytest.mark.parametrize("mag", [1e-3, 1.0, 37.0, 3e4])
+@pytest.mark.parametrize("n", [16 * 576 * 3, 16 * 576 * 3 - 5, 999])
+def test_dynamic_q_cast_bit_exact(gpu, mag, n):
+    rng = np.random.default_rng(2800 + n)
+    x = torch.from_numpy(rng.standard_normal(n).astype(np.float32) * mag).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().astype(np.uint16)
+    bits[: min(n, 40)] = rng.integers(0, 1 << 16, size=min(n, 40))  # every exponent range, NaN / inf included
+    codes, scale = _dyn_cast(gpu, bits)
+    want_codes, want_scale = oracle.quantize_q_dynamic(bits)
+    assert np.float32(scale) == np.float32(want_scale)
+    bad = np.nonzero(codes != want_codes)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first at {bad[0]}: bits {bits[bad[0]]:#06x} got {codes[bad[0]]:#x} want {want_codes[bad[0]]:#x}"
+
+
+def test_dynamic_q_cast_unaligned_view(gpu):
+    rng = np.random.default_rng(2900)
+    x = torch.from_numpy(rng.standard_normal(5000).astype(np.float32) * 3.0).to(torch.bfloat16).to(gpu)
+    src = x[3:-2]  # 6-byte offset: the element-by-element amax path
+    dst = torch.empty(src.numel() + 1, dtype=torch.uint8, device=gpu)[1:]
+    scale = torch.empty(1, dtype=torch.float32, device=gpu)
+    scratch = torch.empty(binding.MLA_QUANT_DYNAMIC_SCRATCH_BYTES, dtype=torch.uint8, device=gpu)
+    binding.mla_decode_quantize_q_dynamic(src, dst, scale, scratch)
+    torch.cuda.synchronize()
+    want_codes, want_scale = oracle.quantize_q_dynamic(src.cpu().view(torch.int16).numpy())
+    assert float(scale.cpu()[0]) == want_scale
+    assert np.array_equal(dst.cpu().numpy(), want_codes)
+
+
+def test_dynamic_q_cast_degenerate(gpu):
+    codes, scale = _dyn_cast(gpu, np.array([0x0000, 0x8000, 0x0000], dtype=np.uint16))
+    assert scale == 1.0 and codes.tolist() == [0x00, 0x80, 0x00]
+    codes, scale = _dyn_cast(gpu, np.zeros(0, dtype=np.uint16))
+    assert scale == 1.0 and codes.size == 0
+    bits = np.array([0x3F80, 0xC000, 0x3F00, 0x7F80, 0xFF80, 0x7FC1, 0xFFC1], dtype=np.uint16)  # 1, -2, .5, inf...
+    codes, scale = _dyn_cast(gpu, bits)
+    assert np.float32(scale) == np.float32(2.0) / np.float32(448.0)
+    assert codes.tolist()[1] == 0xFE and codes.tolist()[3:] == [0x7F, 0xFF, 0x7F, 0xFF]
+
+
+def test_decode_with_dynamic_q_scale(gpu):
+    spec = synth.CaseSpec(batch=4, q_dtype="fp8", kv_dtype="fp8", lengths=[7, 300, 1500, 64], permuted=True,
+                          seed=3000)
+    case = synth.make_case(spec)
+    case.q_bf16 = (case.q_bf16.float() * 60.0).to(torch.bfloat16)  # |q| up to ~300: the scale is not 1
+    dc = DevCase(case, gpu)
+    scratch = torch.empty(binding.MLA_QUANT_DYNAMIC_SCRATCH_BYTES, dtype=torch.uint8, device=gpu)
+    binding.mla_decode_quantize_q_dynamic(dc.q_bf16, dc.q, dc.q_scale, scratch)
+    codes, q_scale = oracle.quantize_q_dynamic(case.q_bits().numpy())
+    assert float(dc.q_scale.cpu()[0]) == q_scale and q_scale != 1.0
+    assert np.array_equal(dc.q.cpu().numpy().reshape(codes.shape), codes)
+    ref = oracle.mla_decode(codes, case.kv_bits().numpy(), case.qo_indptr.numpy(), case.kv_indptr.numpy(),
+                            case.kv_indices.numpy(), q_dtype="fp8", kv_dtype="fp8", q_scale=q_scale,
+                            kv_scale=float(case.kv_scale[0]))
+    for units in (1, 64):
+        out = dc.run(num_units=units, min_chunk=32)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"dynamic q_scale u{units}")
