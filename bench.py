@@ -3,8 +3,10 @@
 A step is one pass of the whole path over one batch: one mla_decode_run
 (work split, split attention and the merge of split partials).  With fp8
 queries the attention kernel casts the bf16 Q itself (step a0 fused); with
---separate-q-cast the step is the standalone cast launch followed by the run.  The plan is made once: it
-does not depend on the sequence lengths.
+--separate-q-cast the step is the standalone cast launch followed by the
+run, and the amax-scaled workload runs the two launches of
+mla_decode_quantize_q_dynamic before it.  The plan is made once: it does not
+depend on the sequence lengths.
 
 Inputs are seeded synthetic tensors of the workload's shapes, resident in HBM
 before the timed region.  The KV pool and its indices are replicated R times
@@ -13,9 +15,12 @@ step cannot be served from the 256 MB last-level cache left warm by the
 previous step.
 
 Throughput is reported as algorithmic HBM bytes per second: KV rows read
-(576 B for fp8, 1152 B for bf16) + 4 B kv_indices per row + Q + bf16 output +
-both indptrs.  The split partials are implementation overhead and are not
-counted; their traffic shows up in the FETCH_SIZE / WRITE_SIZE counters.
+(576 B for fp8, 1152 B for bf16) + 4 B per page index + Q + bf16 output +
+both indptrs (+ the last-page lengths when pages hold several rows).  The
+split partials are implementation overhead and are not counted; their
+traffic shows up in the FETCH_SIZE / WRITE_SIZE counters.  The roofline
+object times the attention launch alone (mla_decode_attend between two HIP
+events on its stream; mla_decode_merge follows outside the events).
 """
 
 from __future__ import annotations
@@ -33,6 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense
+METRIC = "MLA decode µs/call + achieved HBM GB/s (% peak), bs=64 kv=8192 fp8 KV"
 DEFAULT_WORKLOAD = "m_bf16q_fp8kv_b64_kv8192"
 KERNEL_SOURCES = ["mla_decode_paged_split_amd/csrc/mla_device.hpp", "mla_decode_paged_split_amd/csrc/mla_decode.hip"]
 
@@ -45,19 +52,44 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(spec, total_kv: int, q_elt: int) -> int:
+def algorithmic_bytes(spec, case, q_elt: int) -> int:
+    """Bytes one attention launch must move at least: every KV row once, its page index, Q, O, indptrs."""
     kv_elt = 1 if spec.kv_dtype == "fp8" else 2
     B = spec.batch
-    return total_kv * 576 * kv_elt + total_kv * 4 + B * 16 * 576 * q_elt + B * 16 * 512 * 2 + 2 * (B + 1) * 4
+    total_q = case.total_q
+    pages = int(case.kv_indptr[-1])
+    n = case.total_kv * 576 * kv_elt + pages * 4 + total_q * 16 * 576 * q_elt + total_q * 16 * 512 * 2
+    n += 2 * (B + 1) * 4 + (B * 4 if spec.page_size > 1 else 0)
+    return n
 
 
-def workload_label(spec) -> str:
+def mfma_flops(case, causal: bool) -> int:
+    """Multiply-adds of the two contractions (16 heads x (576 + 512) per row each token sees), times 2."""
+    per_row = 2 * 16 * (576 + 512)
+    rows = 0
+    qo = case.qo_indptr.tolist()
+    for b, L in enumerate(case.lengths.tolist()):
+        ql = qo[b + 1] - qo[b]
+        for i in range(ql):
+            rows += max(0, min(L, L - ql + 1 + i)) if causal else L
+    return rows * per_row
+
+
+def workload_label(name, spec, opts) -> str:
     lens = f"kv{spec.kv_len}" if not spec.ragged_max else f"kv U[1,{spec.ragged_max}] permuted"
-    return f"MLA decode b{spec.batch} {lens} {spec.q_dtype}-Q {spec.kv_dtype}-KV page_size=1"
+    extra = []
+    if spec.q_lens is not None:
+        extra.append(f"q_len={max(spec.q_lens)}" + (" causal" if opts.get("causal") else ""))
+    if opts.get("logit_cap"):
+        extra.append(f"logit_cap={opts['logit_cap']}")
+    if opts.get("dynamic_q"):
+        extra.append("amax-scaled Q cast")
+    tail = (" " + " ".join(extra)) if extra else ""
+    return f"{name}: MLA decode b{spec.batch} {lens} {spec.q_dtype}-Q {spec.kv_dtype}-KV page_size={spec.page_size}{tail}"
 
 
-def load_traffic(workload: str, launches_per_step: int):
-    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+def load_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, if it matches the current kernel."""
     path = os.path.join(ROOT, "profiles", f"mla_decode_kernel_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -68,7 +100,7 @@ def load_traffic(workload: str, launches_per_step: int):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, budget_s: float):
+def cpu_baseline(case, opts, budget_s: float):
     """Time the float64 oracle on whole sequences until about budget_s of CPU work."""
     import oracle
 
@@ -78,23 +110,30 @@ def cpu_baseline(case, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    spec = case.spec
     q_bits = case.q_bits().numpy()
-    if case.spec.q_dtype == "fp8":
-        q_bits = oracle.bf16_bits_to_fp8_bits(q_bits)
+    q_scale = None
+    if spec.q_dtype == "fp8":
+        if opts.get("dynamic_q"):
+            q_bits, q_scale = oracle.quantize_q_dynamic(q_bits)
+        else:
+            q_bits, q_scale = oracle.bf16_bits_to_fp8_bits(q_bits), 1.0
     kv_bits = case.kv_bits().numpy()
     qo = case.qo_indptr.numpy()
     kvp = case.kv_indptr.numpy()
     idx = case.kv_indices.numpy()
+    last = case.kv_last_page_len.numpy()
     kv_scale = float(case.kv_scale[0]) if case.kv_scale is not None else None
-    q_scale = 1.0 if case.spec.q_dtype == "fp8" else None
     # whole passes over the batch (at least one sequence, at least one pass when it fits the budget)
     done = []
     passes = 0
     t0 = time.perf_counter()
     while True:
-        for b in range(case.spec.batch):
-            oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype=case.spec.q_dtype, kv_dtype=case.spec.kv_dtype,
-                              q_scale=q_scale, kv_scale=kv_scale, sequences=[b])
+        for b in range(spec.batch):
+            oracle.mla_decode(q_bits, kv_bits, qo, kvp, idx, q_dtype=spec.q_dtype, kv_dtype=spec.kv_dtype,
+                              q_scale=q_scale, kv_scale=kv_scale, sequences=[b], page_size=spec.page_size,
+                              kv_last_page_len=last, causal=bool(opts.get("causal")),
+                              logit_cap=float(opts.get("logit_cap", 0.0)))
             done.append(b)
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -103,12 +142,14 @@ def cpu_baseline(case, budget_s: float):
             continue
         break
     dt = time.perf_counter() - t0
-    rows = int(sum(int(kvp[b + 1] - kvp[b]) for b in done))
-    kv_elt = 1 if case.spec.kv_dtype == "fp8" else 2
-    q_elt = 1 if case.spec.q_dtype == "fp8" else 2
+    lens = case.lengths.numpy()
+    rows = int(sum(int(lens[b]) for b in done))
+    kv_elt = 1 if spec.kv_dtype == "fp8" else 2
+    q_elt = 1 if spec.q_dtype == "fp8" else 2
+    toks = int(sum(int(qo[b + 1] - qo[b]) for b in done))
     nb = len(done)
-    bytes_done = rows * (576 * kv_elt + 4) + nb * (16 * 576 * q_elt + 16 * 512 * 2 + 8)
-    sample = (f"{passes} full passes + {nb - passes * case.spec.batch} sequences of the {case.spec.batch}-sequence "
+    bytes_done = rows * (576 * kv_elt + 4) + toks * (16 * 576 * q_elt + 16 * 512 * 2) + nb * 8
+    sample = (f"{passes} full passes + {nb - passes * spec.batch} sequences of the {spec.batch}-sequence "
               f"batch ({rows} KV rows), float64 numpy, {dt:.1f} s")
     return {
         "value": bytes_done / dt / 1e9,
@@ -116,7 +157,7 @@ def cpu_baseline(case, budget_s: float):
         "cores": int(threads),
         "kind": "oracle",
         "sample": sample,
-        "us_per_call_extrapolated": dt / nb * case.spec.batch * 1e6,
+        "us_per_call_extrapolated": dt / nb * spec.batch * 1e6,
     }
 
 
@@ -164,9 +205,8 @@ def main() -> int:
                           "GBps_read_plus_write": 2 * n / dt / 1e9}))
         return 0
 
-    spec = synth.CONFIGS[args.workload]
+    spec, opts = synth.workload(args.workload)
     case = synth.make_case(spec)
-    total_kv = case.total_kv
     kv_bytes_one = case.kv.numel() * case.kv.element_size()
     R = max(1, min(16, math.ceil(args.rotate_bytes / max(kv_bytes_one, 1))))
 
@@ -175,35 +215,49 @@ def main() -> int:
     idxs = [case.kv_indices.to(dev) for _ in range(R)]
     qo_indptr = case.qo_indptr.to(dev)
     kv_indptr = case.kv_indptr.to(dev)
+    last = case.kv_last_page_len.to(dev) if spec.page_size > 1 else None
     kv_scale = case.kv_scale.to(dev) if case.kv_scale is not None else None
     fp8_q = spec.q_dtype == "fp8"
-    sep_cast = fp8_q and args.separate_q_cast
+    dynamic_q = bool(opts.get("dynamic_q"))
+    sep_cast = fp8_q and (args.separate_q_cast or dynamic_q)
     q_in = torch.empty(q_bf16.shape, dtype=torch.uint8, device=dev) if sep_cast else q_bf16
     q_scale = torch.ones(1, dtype=torch.float32, device=dev) if fp8_q else None
-    out = torch.empty((spec.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+    scratch = torch.empty(binding.MLA_QUANT_DYNAMIC_SCRATCH_BYTES, dtype=torch.uint8, device=dev)
+    out = torch.empty((case.total_q, 16, 512), dtype=torch.bfloat16, device=dev)
     flags = args.flags | (binding.MLA_FLAG_FUSED_Q_CAST if fp8_q and not sep_cast else 0)
+    causal = bool(opts.get("causal"))
+    flags |= binding.MLA_FLAG_CAUSAL if causal else 0
+    max_q = max(spec.q_lens) if spec.q_lens is not None else 1
     dec = binding.Decoder(spec.batch, spec.q_dtype, spec.kv_dtype, dev, num_units=args.num_units,
-                          min_chunk=args.min_chunk, flags=flags)
+                          min_chunk=args.min_chunk, flags=flags, page_size=spec.page_size,
+                          max_q_len=max_q if max_q > 1 else 0, total_q=case.total_q,
+                          logit_cap=float(opts.get("logit_cap", 0.0)))
     sm_scale = 1.0 / 24.0
     stream = torch.cuda.current_stream()
 
     def step(i: int, ev=None):
         r = i % R
-        if sep_cast:
+        if dynamic_q:
+            binding.mla_decode_quantize_q_dynamic(q_bf16, q_in, q_scale, scratch, stream)
+        elif sep_cast:
             binding.mla_decode_quantize_q(q_bf16, q_in, stream)
         if ev is not None:
             ev[0].record(stream)
-        dec.run(q_in, kvs[r], qo_indptr, kv_indptr, idxs[r], q_scale, kv_scale, sm_scale, out, stream)
+        binding.mla_decode_attend(dec.plan, q_in, kvs[r], qo_indptr, kv_indptr, idxs[r], last, q_scale, kv_scale,
+                                  sm_scale, out, stream)
         if ev is not None:
             ev[1].record(stream)
+        binding.mla_decode_merge(dec.plan, qo_indptr, kv_indptr, out, stream)
 
+    # every event is created before the warm-up, so no host work idles the GPU between the two timed regions
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     # timed region 1: whole steps back to back
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
@@ -215,7 +269,6 @@ def main() -> int:
     ms_per_step = ms_total / args.steps
 
     # timed region 2: the attention launch alone, bracketed by events on its stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
@@ -224,14 +277,21 @@ def main() -> int:
     kern_med_ms = kern_ms[len(kern_ms) // 2]
 
     q_elt = 1 if sep_cast else 2  # the attention launch reads fp8 Q, or bf16 Q it casts itself
-    alg_bytes = algorithmic_bytes(spec, total_kv, q_elt)
-    step_bytes = alg_bytes + (q_bf16.numel() * 3 if sep_cast else 0)
+    alg_bytes = algorithmic_bytes(spec, case, q_elt)
+    q_prep = 0
+    if dynamic_q:
+        q_prep = q_bf16.numel() * 5  # amax pass reads 2 B, cast pass reads 2 B and writes 1 B per value
+    elif sep_cast:
+        q_prep = q_bf16.numel() * 3
+    step_bytes = alg_bytes + q_prep
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, 1)
+    flops = mfma_flops(case, causal)
+    mfma_dtype = "fp8" if spec.q_dtype == "fp8" else "bf16"  # QK in fp8 for a8w8; P.V always bf16
+    mfma_tflops = flops / (kern_avg_ms * 1e-3) / 1e12
 
     res = {
-        "metric": "MLA decode µs/call + achieved HBM GB/s (% peak), bs=64 kv=8192 fp8 KV",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -242,25 +302,28 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not fp8_q else "fp8",
+        "dtype": "fp8" if fp8_q else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": workload_label(spec),
+            "workload": workload_label(args.workload, spec, opts),
             "batch": spec.batch,
-            "q_seq_len": 1,
+            "q_seq_len": max_q,
             "kv_len": spec.kv_len if not spec.ragged_max else f"U[1,{spec.ragged_max}]",
-            "total_kv_rows": total_kv,
+            "total_kv_rows": case.total_kv,
             "q_dtype": spec.q_dtype,
             "kv_dtype": spec.kv_dtype,
             "heads": 16,
             "qk_dim": 576,
             "v_dim": 512,
-            "page_size": 1,
+            "page_size": spec.page_size,
+            "causal": causal,
+            "logit_cap": float(opts.get("logit_cap", 0.0)),
             "kv_copies_rotated": R,
             "num_units": int(dec.plan.params.num_units),
             "min_chunk": int(dec.plan.params.min_chunk),
-            "fused_merge": bool(args.flags & 1),
-            "q_cast": ("separate launch" if sep_cast else "in the attention kernel") if fp8_q else None,
+            "fused_merge": bool(args.flags & binding.MLA_FLAG_FUSED_MERGE),
+            "q_cast": (("amax-scaled, two launches" if dynamic_q else "separate launch") if sep_cast
+                       else "in the attention kernel") if fp8_q else None,
         },
         "roofline": {
             "bound": "hbm",
@@ -268,17 +331,24 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
+            "traffic": load_traffic(args.workload),
             "kernel": "mla_decode_kernel",
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
             "kernel_median_us": round(kern_med_ms * 1e3, 2),
+            "mfma": {
+                "flops_per_launch": flops,
+                "achieved_tflops": round(mfma_tflops, 1),
+                "peak_tflops": PEAK_MFMA_TFLOPS[mfma_dtype],
+                "dtype": mfma_dtype,
+                "frac": round(mfma_tflops / PEAK_MFMA_TFLOPS[mfma_dtype], 4),
+            },
         },
         "wall_s_timed": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(case, opts, args.cpu_budget)
     print(json.dumps(res), flush=True)
     return 0
 

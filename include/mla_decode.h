@@ -169,6 +169,25 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
                           hipStream_t stream);
 
 /*
+ * The two launches of one decode step, for callers that order or time them
+ * separately (the pages call the stage-1 kernel and the reduce directly,
+ * submission 690201).  mla_decode_attend enqueues the split attention: it
+ * writes the rows of sequences that one workgroup finishes, and the float32
+ * partials of split sequences into the workspace (merged in the same launch
+ * with MLA_FLAG_FUSED_MERGE).  mla_decode_merge enqueues the merge of those
+ * partials into `out` (nothing with MLA_FLAG_FUSED_MERGE); it must follow
+ * mla_decode_attend on the same stream with the same plan, qo_indptr,
+ * kv_indptr and out, before the workspace is used again.  Arguments as for
+ * mla_decode_run_paged, which is these two calls in order.
+ */
+mla_status mla_decode_attend(const mla_decode_plan_t* plan, const void* q, const void* kv,
+                             const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                             const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
+                             float sm_scale, void* out, hipStream_t stream);
+mla_status mla_decode_merge(const mla_decode_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            void* out, hipStream_t stream);
+
+/*
  * mla_decode_run with the rows of each sequence's last page given by
  * kv_last_page_len[b] (device int32 [batch], clamped into [1, page_size];
  * NULL: every page full), as the pages pass kv_last_page_lens next to

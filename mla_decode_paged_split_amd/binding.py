@@ -35,6 +35,8 @@ __all__ = [
     "mla_decode_plan",
     "mla_decode_run",
     "mla_decode_run_paged",
+    "mla_decode_attend",
+    "mla_decode_merge",
     "mla_decode_quantize_q",
     "mla_decode_quantize_q_dynamic",
     "MLA_QUANT_DYNAMIC_SCRATCH_BYTES",
@@ -119,6 +121,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run_paged.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                            vp]
         L.mla_decode_run_paged.restype = ctypes.c_int
+        L.mla_decode_attend.argtypes = L.mla_decode_run_paged.argtypes
+        L.mla_decode_attend.restype = ctypes.c_int
+        L.mla_decode_merge.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp]
+        L.mla_decode_merge.restype = ctypes.c_int
         L.mla_decode_quantize_q.argtypes = [vp, vp, i64, vp]
         L.mla_decode_quantize_q.restype = ctypes.c_int
         L.mla_decode_quantize_q_dynamic.argtypes = [vp, vp, vp, vp, sz, i64, vp]
@@ -220,6 +226,25 @@ def mla_decode_run_paged(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor,
                                       _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(q_scale), _ptr(kv_scale),
                                       float(sm_scale), _ptr(out), _stream(stream))
     _check(code, "mla_decode_run_paged")
+
+
+def mla_decode_attend(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
+                      kv_indptr: torch.Tensor, kv_indices: torch.Tensor, kv_last_page_len: Optional[torch.Tensor],
+                      q_scale: Optional[torch.Tensor], kv_scale: Optional[torch.Tensor], sm_scale: float,
+                      out: torch.Tensor, stream=None) -> None:
+    _check_index_args(out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                      kv_last_page_len=kv_last_page_len)
+    code = lib().mla_decode_attend(ctypes.byref(plan), _ptr(q), _ptr(kv), _ptr(qo_indptr), _ptr(kv_indptr),
+                                   _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(q_scale), _ptr(kv_scale),
+                                   float(sm_scale), _ptr(out), _stream(stream))
+    _check(code, "mla_decode_attend")
+
+
+def mla_decode_merge(plan: MlaDecodePlan, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, out: torch.Tensor,
+                     stream=None) -> None:
+    _check_index_args(out, qo_indptr=qo_indptr, kv_indptr=kv_indptr)
+    code = lib().mla_decode_merge(ctypes.byref(plan), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(out), _stream(stream))
+    _check(code, "mla_decode_merge")
 
 
 def mla_decode_quantize_q(q_bf16: torch.Tensor, q_fp8: torch.Tensor, stream=None) -> None:

@@ -113,6 +113,38 @@ hipError_t launch_attention(const mla::Args& a, hipStream_t stream) {
   return launch_attention_ql<QT, KT, 1, true>(a, stream);
 }
 
+// The plan-derived launch arguments shared by the attention and merge
+// launches; checks the plan and the pointers both launches read.
+mla_status make_args(const mla_decode_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
+                     mla::Args* a) {
+  if (plan == nullptr) return MLA_ERR_INVALID_ARG;
+  const mla_decode_params& p = plan->params;
+  mla_status st = validate_params(&p);
+  if (st != MLA_OK) return st;
+  if (p.num_units < 1 || p.min_chunk < mla::kSplitAlign) return MLA_ERR_INVALID_ARG;
+  if (plan->workspace == nullptr || plan->workspace_bytes < layout_for(&p, p.num_units).total)
+    return MLA_ERR_WORKSPACE;
+  if (qo_indptr == nullptr || kv_indptr == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  uint8_t* ws = static_cast<uint8_t*>(plan->workspace);
+  memset(a, 0, sizeof(*a));
+  a->qo_indptr = qo_indptr;
+  a->kv_indptr = kv_indptr;
+  a->logit_cap = p.logit_cap;
+  a->out = static_cast<uint16_t*>(out);
+  a->part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
+  a->part_lse = reinterpret_cast<float*>(ws + plan->off_part_lse);
+  a->counters = reinterpret_cast<int32_t*>(ws + plan->off_counters);
+  a->batch = p.batch;
+  a->units = p.num_units;
+  a->min_chunk = p.min_chunk;
+  a->page_shift = ilog2(p.page_size);
+  a->max_q_len = max_q_of(&p);
+  a->causal = (p.flags & MLA_FLAG_CAUSAL) ? 1 : 0;
+  a->fused = (p.flags & MLA_FLAG_FUSED_MERGE) ? 1 : 0;
+  a->q_cast = (p.flags & MLA_FLAG_FUSED_Q_CAST) ? 1 : 0;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,48 +213,25 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
   return MLA_OK;
 }
 
-mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, const void* kv,
-                                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
-                                const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
-                                float sm_scale, void* out, hipStream_t stream) {
-  if (plan == nullptr) return MLA_ERR_INVALID_ARG;
-  const mla_decode_params& p = plan->params;
-  mla_status st = validate_params(&p);
+mla_status mla_decode_attend(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,
+                             const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                             const float* q_scale, const float* kv_scale, float sm_scale, void* out,
+                             hipStream_t stream) {
+  mla::Args a;
+  mla_status st = make_args(plan, qo_indptr, kv_indptr, out, &a);
   if (st != MLA_OK) return st;
-  if (p.num_units < 1 || p.min_chunk < mla::kSplitAlign) return MLA_ERR_INVALID_ARG;
-  if (plan->workspace == nullptr || plan->workspace_bytes < layout_for(&p, p.num_units).total)
-    return MLA_ERR_WORKSPACE;
-  if (q == nullptr || kv == nullptr || qo_indptr == nullptr || kv_indptr == nullptr || kv_indices == nullptr ||
-      out == nullptr)
-    return MLA_ERR_INVALID_ARG;
+  const mla_decode_params& p = plan->params;
+  if (q == nullptr || kv == nullptr || kv_indices == nullptr) return MLA_ERR_INVALID_ARG;
   if (p.q_dtype == MLA_DTYPE_FP8_E4M3FN && q_scale == nullptr) return MLA_ERR_INVALID_ARG;
   if (p.kv_dtype == MLA_DTYPE_FP8_E4M3FN && kv_scale == nullptr) return MLA_ERR_INVALID_ARG;
   if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return MLA_ERR_INVALID_ARG;
-
-  uint8_t* ws = static_cast<uint8_t*>(plan->workspace);
-  mla::Args a;
   a.q = q;
   a.kv = kv;
-  a.qo_indptr = qo_indptr;
-  a.kv_indptr = kv_indptr;
   a.kv_indices = kv_indices;
   a.kv_last_page_len = kv_last_page_len;
   a.q_scale = q_scale;
   a.kv_scale = kv_scale;
   a.sm_scale = sm_scale;
-  a.logit_cap = p.logit_cap;
-  a.out = static_cast<uint16_t*>(out);
-  a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
-  a.part_lse = reinterpret_cast<float*>(ws + plan->off_part_lse);
-  a.counters = reinterpret_cast<int32_t*>(ws + plan->off_counters);
-  a.batch = p.batch;
-  a.units = p.num_units;
-  a.min_chunk = p.min_chunk;
-  a.page_shift = ilog2(p.page_size);
-  a.max_q_len = max_q_of(&p);
-  a.causal = (p.flags & MLA_FLAG_CAUSAL) ? 1 : 0;
-  a.fused = (p.flags & MLA_FLAG_FUSED_MERGE) ? 1 : 0;
-  a.q_cast = (p.flags & MLA_FLAG_FUSED_Q_CAST) ? 1 : 0;
 
   hipError_t err;
   if (p.q_dtype == MLA_DTYPE_BF16 && p.kv_dtype == MLA_DTYPE_BF16)
@@ -231,13 +240,27 @@ mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, co
     err = launch_attention<mla::Dt::BF16, mla::Dt::FP8>(a, stream);
   else
     err = launch_attention<mla::Dt::FP8, mla::Dt::FP8>(a, stream);
-  if (err != hipSuccess) return MLA_ERR_HIP;
-  if (!a.fused) {
-    hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(p.batch, mla::kHeads, a.max_q_len), dim3(64), 0, stream,
-                       a);
-    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
-  }
-  return MLA_OK;
+  return err == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_merge(const mla_decode_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            void* out, hipStream_t stream) {
+  mla::Args a;
+  mla_status st = make_args(plan, qo_indptr, kv_indptr, out, &a);
+  if (st != MLA_OK) return st;
+  if (a.fused) return MLA_OK;  // the attention launch merged already
+  hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(a.batch, mla::kHeads, a.max_q_len), dim3(64), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, const void* kv,
+                                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
+                                float sm_scale, void* out, hipStream_t stream) {
+  mla_status st = mla_decode_attend(plan, q, kv, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_scale,
+                                    kv_scale, sm_scale, out, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_merge(plan, qo_indptr, kv_indptr, out, stream);
 }
 
 mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,

@@ -11,9 +11,11 @@ Two kinds of summary:
   bench can drop the figure once the kernel changes).
 
 Usage:
-  python -m mla_decode_paged_split_amd.profile_summary trace <stats.csv> <out.md> "<command>"
+  python -m mla_decode_paged_split_amd.profile_summary trace <stats.csv> <out.md> "<command>" \
+      [<trace.csv> <timed steps> <bench log>]
   python -m mla_decode_paged_split_amd.profile_summary pmc <workload> <fetch.csv> <write.csv> \
       <copy_fetch.csv> <copy_write.csv> <algorithmic_bytes> <out.json> "<commands>"
+  python -m mla_decode_paged_split_amd.profile_summary mfma <counters.csv> <out.md> "<command>" <flops> <peak>
 """
 
 from __future__ import annotations
@@ -39,7 +41,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def trace_summary(stats_csv: str, out_md: str, command: str) -> None:
+def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | None = None, steps: int = 0,
+                  bench_log: str | None = None) -> None:
+    """The --stats table, plus (with the per-dispatch trace) the attention launches of the bench's last
+    timed region, which are the launches its HIP events time, and the bench's own line from that run."""
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [
         "# Kernel trace summary",
@@ -47,6 +52,8 @@ def trace_summary(stats_csv: str, out_md: str, command: str) -> None:
         f"Command: `{command}`",
         "",
         f"Kernel sources hash: `{kernel_source_hash()}`",
+        "",
+        "All dispatches (warm-up and both timed regions):",
         "",
         "| kernel | calls | avg us | min us | max us | share |",
         "|---|---|---|---|---|---|",
@@ -56,6 +63,27 @@ def trace_summary(stats_csv: str, out_md: str, command: str) -> None:
             f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
             f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |"
         )
+    if trace_csv and steps > 0:
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(open(trace_csv))
+             if ATTENTION in r["Kernel_Name"]]
+        last = d[-steps:]
+        lines += [
+            "",
+            f"Attention launches of the event-timed region (the last {len(last)} of {len(d)}): "
+            f"mean {statistics.mean(last):.2f} us, median {statistics.median(last):.2f} us, "
+            f"min {min(last):.2f} us, max {max(last):.2f} us.",
+        ]
+    if bench_log:
+        for line in open(bench_log):
+            if line.startswith("{") and '"roofline"' in line:
+                b = json.loads(line)
+                r = b["roofline"]
+                lines += [
+                    "",
+                    f"The bench line of the same profiled run: step {b['us_per_call']} us, attention launch by HIP "
+                    f"events mean {r['kernel_avg_us']} us / median {r['kernel_median_us']} us (the events also "
+                    f"enclose the profiler's dispatch handling), roofline frac {r['frac']}.",
+                ]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -106,10 +134,47 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
         fh.write("\n")
 
 
+def mfma_summary(counter_csv: str, out_md: str, command: str, flops_per_launch: int, mfma_peak_tflops: float) -> None:
+    """MFMA busy share of the attention launch from SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE.
+
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so GRBM_GUI_ACTIVE / 8 is the launch's length in GPU cycles;
+    SQ_VALU_MFMA_BUSY_CYCLES is taken as summed over the 1024 SIMDs (256 CUs x 4), so the busy share is
+    MFMA_BUSY / (1024 * GRBM_GUI_ACTIVE / 8).  The algorithmic rate (flops / launch time / peak) is the
+    cross-check of that reading."""
+    vals: dict = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if ATTENTION in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    cycles = med["GRBM_GUI_ACTIVE"] / 8
+    busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cycles)
+    lines = [
+        "# MFMA utilisation of the attention launch",
+        "",
+        f"Command: `{command}`",
+        "",
+        f"Kernel sources hash: `{kernel_source_hash()}`",
+        "",
+        "| counter | median per dispatch |",
+        "|---|---|",
+    ] + [f"| {k} | {v:.0f} |" for k, v in sorted(med.items())] + [
+        "",
+        f"Launch length {cycles:.0f} GPU cycles (GRBM_GUI_ACTIVE / 8 XCDs); MFMA busy share "
+        f"{busy:.3f} = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles).",
+        f"Algorithmic: {flops_per_launch} flops per launch; at the launch length above and 2.4 GHz that is "
+        f"{flops_per_launch / (cycles / 2.4e9) / 1e12:.0f} TFLOP/s, {flops_per_launch / (cycles / 2.4e9) / 1e12 / mfma_peak_tflops:.3f} "
+        f"of the {mfma_peak_tflops:.0f} TFLOP/s dense peak of the P.V dtype.",
+    ]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     kind = sys.argv[1]
     if kind == "trace":
-        trace_summary(sys.argv[2], sys.argv[3], sys.argv[4])
+        trace_summary(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:6] or [None]),
+                      int(sys.argv[6]) if len(sys.argv) > 6 else 0, *(sys.argv[7:8] or [None]))
+    elif kind == "mfma":
+        mfma_summary(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), float(sys.argv[6]))
     elif kind == "pmc":
         pmc_summary(sys.argv[2], *sys.argv[3:7], int(sys.argv[7]), sys.argv[8], sys.argv[9])
     else:

@@ -35,7 +35,7 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["CaseSpec", "Case", "CONFIGS", "make_case", "config_spec"]
+__all__ = ["CaseSpec", "Case", "CONFIGS", "FEATURE_WORKLOADS", "make_case", "config_spec", "workload"]
 
 NUM_HEADS = 16
 QK_DIM = 576
@@ -172,5 +172,32 @@ CONFIGS = {
 }
 
 
+# The widened forms at the headline shape (64 sequences of 8192 rows, fp8
+# KV): pages of 16 rows, the amax-scaled Q cast, two causal query tokens per
+# sequence, and a soft-cap of 30.  Each entry: the case and how to run it.
+FEATURE_WORKLOADS = {
+    "f1_paged16_bf16q_fp8kv_b64_kv8192": (
+        CaseSpec(batch=64, q_dtype="bf16", kv_dtype="fp8", kv_len=8192, permuted=True, page_size=16, seed=7000),
+        {}),
+    "f2_dynq_a8w8_b64_kv8192": (
+        CaseSpec(batch=64, q_dtype="fp8", kv_dtype="fp8", kv_len=8192, seed=6000), {"dynamic_q": True}),
+    "f3_mtp2_causal_bf16q_fp8kv_b64_kv8192": (
+        CaseSpec(batch=64, q_dtype="bf16", kv_dtype="fp8", kv_len=8192, q_lens=[2] * 64, seed=7100),
+        {"causal": True}),
+    "f3_mtp2_causal_a8w8_b64_kv8192": (
+        CaseSpec(batch=64, q_dtype="fp8", kv_dtype="fp8", kv_len=8192, q_lens=[2] * 64, seed=7100),
+        {"causal": True}),
+    "f4_cap30_bf16q_fp8kv_b64_kv8192": (
+        CaseSpec(batch=64, q_dtype="bf16", kv_dtype="fp8", kv_len=8192, seed=6000), {"logit_cap": 30.0}),
+}
+
+
 def config_spec(name: str) -> CaseSpec:
     return CONFIGS[name]
+
+
+def workload(name: str):
+    """(CaseSpec, run options) of a named workload: a decode configuration or a widened form."""
+    if name in CONFIGS:
+        return CONFIGS[name], {}
+    return FEATURE_WORKLOADS[name]

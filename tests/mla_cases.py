@@ -77,12 +77,18 @@ class DevCase:
         return out
 
 
-def oracle_ref(case: synth.Case, sequences=None, causal: bool = False, logit_cap: float = 0.0) -> np.ndarray:
-    """float64 oracle on the same host bytes (fp8 Q from the oracle's own encoder)."""
+def oracle_ref(case: synth.Case, sequences=None, causal: bool = False, logit_cap: float = 0.0,
+               q_fp8=None) -> np.ndarray:
+    """float64 oracle on the same host bytes (fp8 Q from the oracle's own encoder with a unit scale,
+    or the given (codes, q_scale))."""
     q_bits = case.q_bits().numpy()
     if case.spec.q_dtype == "fp8":
-        q_bits = oracle.bf16_bits_to_fp8_bits(q_bits)
-        q_scale = 1.0
+        if q_fp8 is not None:
+            q_bits, q_scale = q_fp8
+            q_bits = np.asarray(q_bits).reshape(case.q_bf16.shape)
+        else:
+            q_bits = oracle.bf16_bits_to_fp8_bits(q_bits)
+            q_scale = 1.0
     else:
         q_scale = None
     kv_scale = float(case.kv_scale[0]) if case.kv_scale is not None else None

@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["mla_decode_workspace_size", "mla_decode_plan", "mla_decode_run", "mla_decode_run_paged",
-              "mla_decode_quantize_q", "mla_decode_quantize_q_dynamic", "mla_decode_reduce", "mla_status_string",
+              "mla_decode_attend", "mla_decode_merge", "mla_decode_quantize_q", "mla_decode_quantize_q_dynamic", "mla_decode_reduce", "mla_status_string",
               "mla_decode_abi_version"]:
         assert n in names
 
@@ -157,6 +157,12 @@ def test_run_rejects_bad_arguments_before_any_hip_call():
     unresolved = _fake_plan()
     unresolved.params.min_chunk = 0
     assert run(unresolved) == B.MLA_ERR_INVALID_ARG
+    # the two halves check the same things before any HIP call
+    assert L.mla_decode_attend(ctypes.byref(plan), None, 4096, 4096, 4096, 4096, None, None, ok_scale, 1 / 24,
+                               4096, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(ctypes.byref(plan), 4096, None, 4096, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(None, 4096, 4096, 4096, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(ctypes.byref(small), 4096, 4096, 4096, None) == B.MLA_ERR_WORKSPACE
     del ptrs
 
 
