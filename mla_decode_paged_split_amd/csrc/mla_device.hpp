@@ -240,9 +240,22 @@ __device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w) {
 // C pages, i.e. C * page_size rows except where a sequence's last page is
 // part-filled.  C is a multiple of max(1, 32 / page_size) and at least
 // min_chunk rows' worth of pages.
+//
+// When the sequences are short on average (fewer than kCostMinAvgRows rows),
+// every sequence also carries a fixed cost of kPieceCostRows rows: sequence b
+// occupies [kv_indptr[b] - base + cost * b, ... + its positions) of a "cost
+// space" whose gaps belong to no one, and the shares cut that space.  Each
+// piece a workgroup walks has a fixed price (a ring start, the Q load, the
+// finish) of about three tiles, so without the term a share of many short
+// sequences serialises them all on one workgroup.  With long sequences the
+// cost is 0 and the space is the positions themselves.
+constexpr int kPieceCostRows = 192;
+constexpr int kCostMinAvgRows = 1024;
+
 struct Geo {
   int32_t base;   // kv_indptr[0]
-  int32_t total;  // N index positions over all sequences
+  int32_t cost;   // positions of cost per sequence (0: none)
+  int32_t total;  // extent of the split space: N index positions + cost * batch
   int32_t chunk;  // C positions per workgroup share
   int32_t n_wg;   // shares in use (>= 1)
 };
@@ -250,7 +263,9 @@ struct Geo {
 __device__ __forceinline__ Geo make_geo(const int32_t* kv_indptr, int batch, int units, int min_chunk, int sh) {
   Geo g;
   g.base = kv_indptr[0];
-  g.total = kv_indptr[batch] - g.base;
+  const int pos = kv_indptr[batch] - g.base;
+  g.cost = ((int64_t)pos < (int64_t)batch * max(1, kCostMinAvgRows >> sh)) ? max(1, kPieceCostRows >> sh) : 0;
+  g.total = pos + g.cost * batch;
   const int align = max(1, kSplitAlign >> sh);
   const int min_pos = max(1, min_chunk >> sh);
   int64_t c = ((int64_t)g.total + units - 1) / units;
@@ -262,8 +277,8 @@ __device__ __forceinline__ Geo make_geo(const int32_t* kv_indptr, int batch, int
   return g;
 }
 
-// Partial slot of the i-th piece of a sequence occupying row-space [st, en)
-// (en > st).  Workgroup k writes the piece of its first sequence to slot 2k
+// Partial slot of the i-th piece of a sequence occupying [st, en) of the
+// split space (en > st).  Workgroup k writes the piece of its first sequence to slot 2k
 // and the piece of its last sequence to slot 2k+1; a sequence that starts
 // exactly at a share boundary is the first sequence of that share.
 __device__ __forceinline__ int piece_slot(int st, int chunk, int i) {
@@ -847,12 +862,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   logit.k2 = a.logit_cap * kLog2e;
   const float out_mul = ks;
 
-  // The first piece always starts at the share start (the sequence holding
-  // position lo begins at or before it), so its ring can be started now,
-  // clamped to the share's pages, while the scan below finds the sequences.
+  // Without the per-sequence cost the first piece always starts at the share
+  // start (the sequence holding position lo begins at or before it), so its
+  // ring can be started now, clamped to the share's pages, while the scan
+  // below finds the sequences.  With it the share may start in a gap.
+  const bool primed = geo.cost == 0;
   Ring<KT, ring_depth<QT, KT, QL>()> ring;
-  issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
-  issue_ring_rows<KT>(a.kv, (hi - lo) << sh, sh, ring);
+  if (primed) {
+    issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
+    issue_ring_rows<KT>(a.kv, (hi - lo) << sh, sh, ring);
+  }
 
   if (threadIdx.x == 0) {
     sm.bmin = 0x7fffffff;
@@ -860,8 +879,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   }
   __syncthreads();  // bmin / bmax initialised
   auto scan_one = [&](int j, int ipb, int ipe, int qo, int aux) {
-    const int st = ipb - geo.base;
-    const int en = ipe - geo.base;
+    const int st = ipb - geo.base + geo.cost * j;
+    const int en = st + (ipe - ipb);
     if (en > st) {
       if (st < hi && en > lo) {
         atomicMin(&sm.bmin, j);
@@ -914,8 +933,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       t = a.qo_indptr[b];
       aux = pack_seq_aux(a, t, multi ? a.qo_indptr[b + 1] : 0, paged ? a.kv_last_page_len[b] : 0, paged);
     }
-    const int st = ipb - geo.base;
-    const int en = ipe - geo.base;
+    const int st = ipb - geo.base + geo.cost * b;  // the sequence's positions in the split space
+    const int en = st + (ipe - ipb);
     if (en <= st) continue;
     const int q_len = aux >> 16;
     const int n_rows = ((en - st - 1) << sh) + (aux & 0xFFFF);  // the last page may be part-filled
@@ -927,7 +946,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
     const int nrows = min((s_hi - st) << sh, n_rows) - r0;
     for (int tau0 = 0; tau0 < q_len; tau0 += QL) {
       Piece<QL> pc;
-      pc.ip0 = s_lo + geo.base;
+      pc.ip0 = ipb + (s_lo - st);
       pc.nrows = nrows;
       pc.t0 = t + tau0;
       pc.ntok = min(QL, q_len - tau0);
@@ -939,7 +958,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       }
       pc.slot = complete ? -1 : slot * a.max_q_len + tau0;
       pc.complete = complete;
-      if (b != bmin || tau0 != 0) {
+      if (!primed || b != bmin || tau0 != 0) {
         issue_ring_indices(a.kv_indices, pc.ip0, nrows, sh, ring);
         issue_ring_rows<KT>(a.kv, nrows, sh, ring);
       }
@@ -977,8 +996,8 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int h = blockIdx.y;
   const int tau = blockIdx.z;
   const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, a.page_shift);
-  const int st = a.kv_indptr[b] - geo.base;
-  const int en = a.kv_indptr[b + 1] - geo.base;
+  const int st = a.kv_indptr[b] - geo.base + geo.cost * b;
+  const int en = st + (a.kv_indptr[b + 1] - a.kv_indptr[b]);
   if (en <= st) return;
   const int qo = a.qo_indptr[b];
   if (a.max_q_len > 1) {

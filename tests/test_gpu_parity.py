@@ -6,6 +6,8 @@ than 64 pieces per sequence).  Invariants that need no oracle are checked too:
 split count, pool permutation, determinism, empty sequences, closed forms.
 """
 
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -246,3 +248,87 @@ def test_fused_q_cast_positive_nan_fallback(gpu):
     assert torch.equal(sep.view(torch.int16), fused.view(torch.int16))
     ok = torch.isfinite(fused.float())
     assert not bool(ok[1, 5].any()) and bool(ok[0].all()) and bool(ok[2].all())
+
+
+# ---------------------------------------------- many short sequences, big batches
+
+def _token_rows(case, seqs):
+    qo = case.qo_indptr.tolist()
+    return [t for b in seqs for t in range(qo[b], qo[b + 1])]
+
+
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_many_short_sequences(gpu, qd, kd):
+    # average length far below 1024 rows: the split charges every sequence a fixed cost, so shares may
+    # begin in the gaps between sequences
+    rng = np.random.default_rng(3100)
+    lens = rng.integers(0, 41, size=600).tolist()
+    spec = synth.CaseSpec(batch=600, q_dtype=qd, kv_dtype=kd, lengths=lens, permuted=True, extra_pool_rows=9,
+                          seed=3100 + PAIRS.index((qd, kd)))
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units, chunk, flags in ((1, 32, 0), (8, 32, 0), (256, 32, 0), (256, 256, 0), (4096, 32, 1)):
+        out = dc.run(num_units=units, min_chunk=chunk, flags=flags)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"short {qd}/{kd} u{units} c{chunk} f{flags}")
+
+
+def test_one_row_sequences_spread_over_workgroups(gpu):
+    spec = synth.CaseSpec(batch=256, q_dtype="bf16", kv_dtype="fp8", lengths=[1] * 256, permuted=True, seed=3200)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    dec = dc.decoder()
+    out = dc.run(dec)
+    torch.cuda.synchronize()
+    assert_parity(oracle_ref(case), to64(out), "one-row sequences")
+    for _ in range(3):
+        dc.run(dec, out)
+    torch.cuda.synchronize()
+    with Timer("10 steps") as tm:
+        for _ in range(10):
+            dc.run(dec, out)
+        torch.cuda.synchronize()
+    per_step_us = (time.time() - tm.t) / 10 * 1e6
+    log(f"  256 one-row sequences: {per_step_us:.1f} us per step (host-timed)")
+    assert per_step_us < 300.0  # one workgroup walking all 256 took ~1300 us
+
+
+@pytest.mark.parametrize("qd,kd", [("bf16", "fp8"), ("fp8", "fp8")])
+def test_batch_beyond_lds_table(gpu, qd, kd):
+    # more than 1024 sequences: the kernel reads the indptrs from memory in the piece loop
+    rng = np.random.default_rng(3300)
+    short = rng.integers(1, 200, size=1500).tolist()  # with the per-sequence cost
+    spec = synth.CaseSpec(batch=1500, q_dtype=qd, kv_dtype=kd, lengths=short, permuted=True, seed=3300)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units in (64, 256):
+        out = dc.run(num_units=units, min_chunk=32)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"big batch short {qd}/{kd} u{units}")
+    long_ = rng.integers(1024, 1400, size=1030).tolist()  # without it
+    spec = synth.CaseSpec(batch=1030, q_dtype=qd, kv_dtype=kd, lengths=long_, permuted=True, seed=3301)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    out = dc.run()
+    torch.cuda.synchronize()
+    seqs = [0, 1, 513, 1023, 1024, 1025, 1029]
+    ref = oracle_ref(case, sequences=seqs)
+    assert_parity(ref[seqs], to64(out)[seqs], f"big batch long {qd}/{kd}")
+
+
+def test_batch_beyond_lds_table_with_tokens(gpu):
+    rng = np.random.default_rng(3400)
+    lens = rng.integers(1, 120, size=1100).tolist()
+    q_lens = rng.integers(1, 4, size=1100).tolist()
+    spec = synth.CaseSpec(batch=1100, q_dtype="fp8", kv_dtype="fp8", lengths=lens, q_lens=q_lens, permuted=True,
+                          page_size=8, seed=3400)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    seqs = [0, 5, 700, 1023, 1024, 1099]
+    ref = oracle_ref(case, sequences=seqs, causal=True)
+    rows = _token_rows(case, seqs)
+    out = dc.run(num_units=256, min_chunk=32, causal=True)
+    torch.cuda.synchronize()
+    assert_parity(ref[rows], to64(out)[rows], "big batch tokens")
