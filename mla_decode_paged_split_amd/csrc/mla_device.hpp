@@ -423,6 +423,7 @@ __device__ __forceinline__ void issue_ring_indices(const int32_t* __restrict__ k
 
 // Start the loads of the ring's first D tiles (in the steady state's slot
 // order, kept by scheduling barriers so the loop's wait counts stay exact).
+// Rows at or past nrows load the first page's slot 0 (never used).
 template <Dt KT, class R>
 __device__ __forceinline__ void issue_ring_rows(const void* kv, int nrows, int sh, R& r) {
   using L = KvLayout<KT>;
@@ -500,6 +501,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   constexpr int kSteps = kQKDim / 32;  // 18
   bf16x8_t qb[QL][QT == Dt::BF16 ? kSteps : 1];
   uint64_t q8[QL][QT == Dt::FP8 ? kSteps : 1];
+  u32x4_t qw[QL][QT == Dt::FP8 ? kSteps : 1];  // bf16 Q of the fused cast, before casting
 #pragma unroll
   for (int q = 0; q < QL; ++q) {
     const size_t qrow = ((size_t)(pc.t0 + (q < pc.ntok ? q : 0)) * kHeads + c16) * kQKDim;
@@ -510,21 +512,28 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         qb[q][s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + d0);
       } else if (!a.q_cast) {
         q8[q][s] = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) + qrow + d0);
-      }
-    }
-    if constexpr (QT == Dt::FP8) {
-      if (a.q_cast) {  // fp8 Q supplied as bf16 (uniform branch)
-        u32x4_t qw[kSteps];
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          const int d0 = ((s >> 1) * 4 + g) * 16 + (s & 1) * 8;
-          qw[s] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + d0);
-        }
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) q8[q][s] = bf16x8_to_e4m3fn(qw[s]);
+      } else {  // fp8 Q supplied as bf16 (uniform branch): same dims, twice the bytes
+        qw[q][s] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + d0);
       }
     }
   }
+  // The ring's rows go out after Q (their page indices were fetched before
+  // the piece began), so Q's loads are not queued behind a ring's worth of
+  // rows, and the fused cast then waits only for Q.  With two tokens the
+  // cast comes first: both tokens' bf16 Q beside the ring would not fit.
+  auto cast_q = [&]() {
+    if constexpr (QT == Dt::FP8) {
+      if (a.q_cast) {
+#pragma unroll
+        for (int q = 0; q < QL; ++q)
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s) q8[q][s] = bf16x8_to_e4m3fn(qw[q][s]);
+      }
+    }
+  };
+  if constexpr (QL > 1) cast_q();
+  issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
+  if constexpr (QL == 1) cast_q();
 
   // tiles up to the furthest row any token of the pass sees
   int maxlim = 0;
@@ -534,7 +543,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
 
-  // the ring arrives primed: tiles 0..D-1 in flight, indices of D..2D-1 loaded
+  // the ring is primed: tiles 0..D-1 in flight, pages of D..2D-1 loaded
   auto& dat = ring.dat;
   auto& idxn = ring.next;
   auto page_index = [&](int tt) { return piece_page(a.kv_indices, pc.ip0, pc.nrows, tt * kTileRows + my_row, sh); };
@@ -846,6 +855,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
     sv[i][3] = a.qo_indptr[j + 1];
     sv[i][4] = last_src[j];
   }
+  __builtin_amdgcn_sched_barrier(0);  // these loads go out before the ring's: the scan waits for them only
   const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, sh);
   const int k = blockIdx.x;
   if (k >= geo.n_wg) return;
@@ -863,15 +873,13 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   const float out_mul = ks;
 
   // Without the per-sequence cost the first piece always starts at the share
-  // start (the sequence holding position lo begins at or before it), so its
-  // ring can be started now, clamped to the share's pages, while the scan
-  // below finds the sequences.  With it the share may start in a gap.
+  // start (the sequence holding position lo begins at or before it), so the
+  // page indices of its ring can be fetched now, clamped to the share's
+  // pages, while the scan below finds the sequences; the piece issues the
+  // rows once its Q is on the way.  With the cost the share may start in a gap.
   const bool primed = geo.cost == 0;
   Ring<KT, ring_depth<QT, KT, QL>()> ring;
-  if (primed) {
-    issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
-    issue_ring_rows<KT>(a.kv, (hi - lo) << sh, sh, ring);
-  }
+  if (primed) issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
 
   if (threadIdx.x == 0) {
     sm.bmin = 0x7fffffff;
@@ -958,10 +966,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       }
       pc.slot = complete ? -1 : slot * a.max_q_len + tau0;
       pc.complete = complete;
-      if (!primed || b != bmin || tau0 != 0) {
-        issue_ring_indices(a.kv_indices, pc.ip0, nrows, sh, ring);
-        issue_ring_rows<KT>(a.kv, nrows, sh, ring);
-      }
+      if (!primed || b != bmin || tau0 != 0) issue_ring_indices(a.kv_indices, pc.ip0, nrows, sh, ring);
       attend_piece<QT, KT, QL, kGeneral>(a, sm, pc, logit, out_mul, ring);
     }
     if (!complete && a.fused && q_len > 0) {
