@@ -100,6 +100,7 @@ struct alignas(16) Smem {
   float mx[2][kWaves][QL][kHeads];  // per-wave tile max of each token and head
   float lsum[kWaves][QL][kHeads];
   int seq[kSeqTable][4];  // kv_indptr[b], kv_indptr[b+1], qo_indptr[b], (tokens << 16) | last-page rows
+                          // of the first kSeqTable sequences
   int bmin;
   int bmax;
   int arrive;
@@ -855,15 +856,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
     sv[i][3] = a.qo_indptr[j + 1];
     sv[i][4] = last_src[j];
   }
-  __builtin_amdgcn_sched_barrier(0);  // these loads go out before the ring's: the scan waits for them only
+  const float qs = (QT == Dt::FP8) ? *a.q_scale : 1.0f;
+  const float ks = (KT == Dt::FP8) ? *a.kv_scale : 1.0f;
+  // these loads go out before the ring's, so using them never waits for the ring's indices
+  __builtin_amdgcn_sched_barrier(0);
   const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, sh);
   const int k = blockIdx.x;
   if (k >= geo.n_wg) return;
   const int lo = k * geo.chunk;
   const int hi = min(lo + geo.chunk, geo.total);
 
-  const float qs = (QT == Dt::FP8) ? *a.q_scale : 1.0f;
-  const float ks = (KT == Dt::FP8) ? *a.kv_scale : 1.0f;
   const float c_nat = a.sm_scale * qs * ks;
   Logit logit;
   logit.c_score = c_nat * kLog2e;
@@ -879,47 +881,48 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   // rows once its Q is on the way.  With the cost the share may start in a gap.
   const bool primed = geo.cost == 0;
   Ring<KT, ring_depth<QT, KT, QL>()> ring;
-  if (primed) issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
 
+  // The first round trip's values go to the LDS sequence table before the
+  // ring's indices are requested, so no register waiting on them stays live
+  // while the indices are in flight (the compiler's wait counts would
+  // otherwise drain the indices at the first join).
+#pragma unroll
+  for (int i = 0; i < kScanPerThread; ++i) {
+    const int j = threadIdx.x + i * kThreads;
+    if (j < a.batch) {
+      sm.seq[j][0] = sv[i][0];
+      sm.seq[j][1] = sv[i][1];
+      sm.seq[j][2] = sv[i][2];
+      sm.seq[j][3] = pack_seq_aux(a, sv[i][2], sv[i][3], sv[i][4], paged);
+    }
+  }
   if (threadIdx.x == 0) {
     sm.bmin = 0x7fffffff;
     sm.bmax = -1;
   }
-  __syncthreads();  // bmin / bmax initialised
-  auto scan_one = [&](int j, int ipb, int ipe, int qo, int aux) {
+  __builtin_amdgcn_sched_barrier(0);
+  if (primed) issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
+  __syncthreads();  // the table and bmin / bmax are in place
+  // (empty sequences are zeroed after the pieces: stores here would enter the
+  // compiler's count of loads in flight and make the prologue wait for all)
+  auto scan_one = [&](int j, int ipb, int ipe) {
     const int st = ipb - geo.base + geo.cost * j;
     const int en = st + (ipe - ipb);
-    if (en > st) {
-      if (st < hi && en > lo) {
-        atomicMin(&sm.bmin, j);
-        atomicMax(&sm.bmax, j);
-      }
-    } else {
-      // an empty sequence belongs to the share holding its position
-      int owner = st / geo.chunk;
-      if (owner > geo.n_wg - 1) owner = geo.n_wg - 1;
-      if (owner == k)
-        for (int r = 0; r < (aux >> 16); ++r) zero_row_by_thread(a.out + (size_t)(qo + r) * kHeads * kVDim);
+    if (en > st && st < hi && en > lo) {
+      atomicMin(&sm.bmin, j);
+      atomicMax(&sm.bmax, j);
     }
   };
 #pragma unroll
   for (int i = 0; i < kScanPerThread; ++i) {
     const int j = threadIdx.x + i * kThreads;
-    if (j < a.batch) {
-      const int aux = pack_seq_aux(a, sv[i][2], sv[i][3], sv[i][4], paged);
-      if constexpr (!kBigBatch) {
-        sm.seq[j][0] = sv[i][0];
-        sm.seq[j][1] = sv[i][1];
-        sm.seq[j][2] = sv[i][2];
-        sm.seq[j][3] = aux;
-      }
-      scan_one(j, sv[i][0], sv[i][1], sv[i][2], aux);
-    }
+    if (j < a.batch) scan_one(j, sm.seq[j][0], sm.seq[j][1]);
   }
-  for (int j = threadIdx.x + kSeqTable; j < a.batch; j += kThreads) {
-    const int qo = a.qo_indptr[j];
-    scan_one(j, a.kv_indptr[j], a.kv_indptr[j + 1], qo,
-             pack_seq_aux(a, qo, multi ? a.qo_indptr[j + 1] : 0, paged ? a.kv_last_page_len[j] : 0, paged));
+  // Sequences past the LDS table (only in the big-batch instantiation: a loop
+  // that merely never runs would still make the compiler drain every load
+  // in flight, the ring's indices included, where its branch rejoins).
+  if constexpr (kBigBatch) {
+    for (int j = threadIdx.x + kSeqTable; j < a.batch; j += kThreads) scan_one(j, a.kv_indptr[j], a.kv_indptr[j + 1]);
   }
   __syncthreads();
   const int bmin = sm.bmin;
@@ -991,6 +994,27 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       }
       __syncthreads();
     }
+  }
+
+  // Empty sequences: zeros, written by the share holding their position.
+  for (int j = threadIdx.x; j < a.batch; j += kThreads) {
+    int ipb, ipe, qo, aux;
+    if constexpr (!kBigBatch) {
+      ipb = sm.seq[j][0];
+      ipe = sm.seq[j][1];
+      qo = sm.seq[j][2];
+      aux = sm.seq[j][3];
+    } else {
+      ipb = a.kv_indptr[j];
+      ipe = a.kv_indptr[j + 1];
+      qo = a.qo_indptr[j];
+      aux = pack_seq_aux(a, qo, multi ? a.qo_indptr[j + 1] : 0, paged ? a.kv_last_page_len[j] : 0, paged);
+    }
+    if (ipe > ipb) continue;
+    int owner = (ipb - geo.base + geo.cost * j) / geo.chunk;
+    if (owner > geo.n_wg - 1) owner = geo.n_wg - 1;
+    if (owner == k)
+      for (int r = 0; r < (aux >> 16); ++r) zero_row_by_thread(a.out + (size_t)(qo + r) * kHeads * kVDim);
   }
 }
 
