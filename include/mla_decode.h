@@ -46,6 +46,11 @@
  * synchronises a stream; all work is enqueued on the stream passed in.
  * One workspace must not be used by two calls that may overlap in time
  * (e.g. on two streams): the calls share its partial buffers and counters.
+ * A run (mla_decode_run, mla_decode_run_paged, or the attend / merge pair)
+ * may be captured into a HIP graph: it enqueues kernels only (no memset, no
+ * allocation, no host synchronisation), and the replayed kernels read the
+ * index arrays at replay time, so sequence lengths may change in place
+ * between replays.
  *
  * Errors: every entry point returns mla_status.  Arguments are validated on
  * the host before any HIP call; a rejected call enqueues nothing.  A HIP

@@ -332,3 +332,47 @@ def test_batch_beyond_lds_table_with_tokens(gpu):
     out = dc.run(num_units=256, min_chunk=32, causal=True)
     torch.cuda.synchronize()
     assert_parity(ref[rows], to64(out)[rows], "big batch tokens")
+
+
+# ----------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("qd,flags", [("bf16", 0), ("bf16", 1), ("fp8", 2)])
+def test_graph_capture_and_replay(gpu, qd, flags):
+    """A captured decode step replays correctly, also after the sequence lengths change in place (the plan
+    does not depend on them), with eager work between the replays; every replay is checked against an
+    eager run on the same inputs."""
+    lens_a = [300, 1, 2049, 700, 64, 1500]
+    lens_b = [10, 900, 33, 2000, 64, 1]
+    spec = synth.CaseSpec(batch=6, q_dtype=qd, kv_dtype="fp8", lengths=lens_a, permuted=True,
+                          extra_pool_rows=3000, seed=3500)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    q = dc.q_bf16 if flags & binding.MLA_FLAG_FUSED_Q_CAST else dc.q
+    dec = dc.decoder(num_units=64, min_chunk=32, flags=flags)
+    indptr_a = dc.kv_indptr.clone()
+    indptr_b = torch.tensor([0] + list(np.cumsum(lens_b)), dtype=torch.int32, device=gpu)
+    out_g = torch.zeros((6, 16, 512), dtype=torch.bfloat16, device=gpu)
+
+    def step(out, indptr):
+        dec.run(q, dc.kv, dc.qo_indptr, indptr, dc.kv_indices, dc.q_scale, dc.kv_scale, oracle.SM_SCALE, out)
+
+    live_indptr = dc.kv_indptr  # the buffer the graph reads
+    step(out_g, live_indptr)  # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out_g, live_indptr)
+    torch.cuda.synchronize()
+    for rep, src in enumerate([indptr_a, indptr_b, indptr_a, indptr_b]):
+        live_indptr.copy_(src)
+        eager = torch.empty_like(out_g)
+        step(eager, src)  # eager work between replays, on the same workspace
+        torch.cuda.synchronize()
+        out_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+    # the last replay ran lengths B: check it against the oracle too
+    case_b = synth.Case(spec, case.q_bf16, case.kv, case.kv_scale, case.qo_indptr, indptr_b.cpu(), case.kv_indices,
+                        torch.tensor(lens_b), case.kv_last_page_len)
+    assert_parity(oracle_ref(case_b), to64(out_g), f"graph lengths B {qd} flags={flags}")
