@@ -93,9 +93,19 @@ struct KvLayout<Dt::BF16> {
 };
 
 
+// Q of a pass staged once per workgroup (fp8 KV only; bf16 KV leaves no LDS
+// for it): one row per token and head, bf16 (1152 B) or fp8 (576 B) values,
+// rows padded to 1168 B.
+constexpr int kQPitch = 1168;
+template <Dt KV, int QL>
+constexpr int q_stage_rows() {
+  return KV == Dt::FP8 ? QL * kHeads : 1;
+}
+
 template <Dt KV, int QL>
 struct alignas(16) Smem {
   uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];  // V part of the current / next tile
+  uint8_t q[q_stage_rows<KV, QL>()][kQPitch];       // the pass's Q (fp8 KV)
   u32x2_t p[2][QL][kWaves][64];     // bf16 weights: token, wave, lane -> 4 rows of one head
   float mx[2][kWaves][QL][kHeads];  // per-wave tile max of each token and head
   float lsum[kWaves][QL][kHeads];
@@ -502,39 +512,71 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   constexpr int kSteps = kQKDim / 32;  // 18
   bf16x8_t qb[QL][QT == Dt::BF16 ? kSteps : 1];
   uint64_t q8[QL][QT == Dt::FP8 ? kSteps : 1];
-  u32x4_t qw[QL][QT == Dt::FP8 ? kSteps : 1];  // bf16 Q of the fused cast, before casting
+  if constexpr (KT == Dt::FP8) {
+    // Q goes through LDS: the workgroup loads each token's 16 rows once (16-byte
+    // pieces over all 256 threads) instead of every wave loading all of them,
+    // so 4x fewer requests sit in front of the ring's rows.  Order: Q loads,
+    // the ring's rows, then Q into LDS (cast to fp8 there when fp8 Q is given
+    // as bf16), a barrier, and each wave's fragments from LDS.
+    const bool src16 = (QT == Dt::BF16) || a.q_cast;  // the source holds bf16 values
+    constexpr int kChunks16 = kHeads * kQKDim * 2 / 16;  // 1152 sixteen-byte pieces of a bf16 Q token
+    constexpr int kPer = (kChunks16 + kThreads - 1) / kThreads;  // 5
+    const int nchunks = src16 ? kChunks16 : kChunks16 / 2;
+    const int per_head = src16 ? kQKDim * 2 / 16 : kQKDim / 16;  // 72 or 36
+    u32x4_t stage[QL][kPer];
 #pragma unroll
-  for (int q = 0; q < QL; ++q) {
-    const size_t qrow = ((size_t)(pc.t0 + (q < pc.ntok ? q : 0)) * kHeads + c16) * kQKDim;
+    for (int q = 0; q < QL; ++q) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) +
+                           (size_t)(pc.t0 + (q < pc.ntok ? q : 0)) * kHeads * kQKDim * (src16 ? 2 : 1);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int d0 = (KT == Dt::FP8) ? (((s >> 1) * 4 + g) * 16 + (s & 1) * 8) : ((s * 4 + g) * 8);
-      if constexpr (QT == Dt::BF16) {
-        qb[q][s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + d0);
-      } else if (!a.q_cast) {
-        q8[q][s] = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) + qrow + d0);
-      } else {  // fp8 Q supplied as bf16 (uniform branch): same dims, twice the bytes
-        qw[q][s] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + d0);
+      for (int i = 0; i < kPer; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        if (c < nchunks) stage[q][i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)c * 16);
       }
     }
+    issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
+#pragma unroll
+    for (int q = 0; q < QL; ++q) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        if (c < nchunks) {
+          const int h = c / per_head;
+          const int off = (c - h * per_head) * 16;  // byte offset in the source row
+          uint8_t* dst = &sm.q[q * kHeads + h][0];
+          if (QT == Dt::FP8 && a.q_cast)
+            *reinterpret_cast<uint64_t*>(dst + off / 2) = bf16x8_to_e4m3fn(stage[q][i]);
+          else
+            *reinterpret_cast<u32x4_t*>(dst + off) = stage[q][i];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QL; ++q) {
+      const uint8_t* row = &sm.q[q * kHeads + c16][0];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int d0 = ((s >> 1) * 4 + g) * 16 + (s & 1) * 8;
+        if constexpr (QT == Dt::BF16)
+          qb[q][s] = *reinterpret_cast<const bf16x8_t*>(row + d0 * 2);
+        else
+          q8[q][s] = *reinterpret_cast<const uint64_t*>(row + d0);
+      }
+    }
+  } else {
+    // bf16 KV (bf16 Q only): every wave loads the whole Q straight into its registers
+    static_assert(QT == Dt::BF16, "fp8 Q is paired with fp8 KV only");
+#pragma unroll
+    for (int q = 0; q < QL; ++q) {
+      const size_t qrow = ((size_t)(pc.t0 + (q < pc.ntok ? q : 0)) * kHeads + c16) * kQKDim;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s)
+        qb[q][s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(a.q) + qrow + (s * 4 + g) * 8);
+    }
+    // the ring's rows go out after Q (their page indices were fetched before the piece began)
+    issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
   }
-  // The ring's rows go out after Q (their page indices were fetched before
-  // the piece began), so Q's loads are not queued behind a ring's worth of
-  // rows, and the fused cast then waits only for Q.  With two tokens the
-  // cast comes first: both tokens' bf16 Q beside the ring would not fit.
-  auto cast_q = [&]() {
-    if constexpr (QT == Dt::FP8) {
-      if (a.q_cast) {
-#pragma unroll
-        for (int q = 0; q < QL; ++q)
-#pragma unroll
-          for (int s = 0; s < kSteps; ++s) q8[q][s] = bf16x8_to_e4m3fn(qw[q][s]);
-      }
-    }
-  };
-  if constexpr (QL > 1) cast_q();
-  issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
-  if constexpr (QL == 1) cast_q();
 
   // tiles up to the furthest row any token of the pass sees
   int maxlim = 0;
