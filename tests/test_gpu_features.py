@@ -204,3 +204,47 @@ def test_decode_with_dynamic_q_scale(gpu):
         out = dc.run(num_units=units, min_chunk=32)
         torch.cuda.synchronize()
         assert_parity(ref, to64(out), f"dynamic q_scale u{units}")
+
+
+# ------------------------------------------------------------------- edge cases
+
+def test_sequences_without_query_tokens(gpu):
+    # q_len 0 for some sequences: nothing is computed for them, the other tokens are unaffected
+    lens, q_lens = [100, 700, 5, 2000], [2, 0, 3, 0]
+    spec = synth.CaseSpec(batch=4, q_dtype="bf16", kv_dtype="fp8", lengths=lens, q_lens=q_lens, permuted=True,
+                          seed=3600)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case, causal=True)
+    for units, flags in ((1, 0), (64, 0), (64, 1)):
+        out = dc.run(num_units=units, min_chunk=32, flags=flags, causal=True)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"q_len 0 u{units} f{flags}")
+
+
+def test_last_page_lengths_out_of_range_are_clamped(gpu):
+    # last-page lengths of 0 and above the page size read as 1 and as a full page, as in the oracle
+    spec = synth.CaseSpec(batch=4, q_dtype="fp8", kv_dtype="fp8", lengths=[40, 9, 64, 17], permuted=True,
+                          page_size=16, extra_pool_rows=64, seed=3700)
+    case = synth.make_case(spec)
+    case.kv_last_page_len = torch.tensor([0, 99, -5, 16], dtype=torch.int32)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)  # the oracle clamps into [1, page_size] itself
+    for units in (1, 8, 64):
+        out = dc.run(num_units=units, min_chunk=32)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"clamped last pages u{units}")
+
+
+@pytest.mark.parametrize("ps", [256, 1024])
+def test_large_pages(gpu, ps):
+    lens = [1, ps - 3, ps + 1, 3 * ps]
+    spec = synth.CaseSpec(batch=4, q_dtype="bf16", kv_dtype="fp8", lengths=lens, permuted=True, page_size=ps,
+                          extra_pool_rows=ps, seed=3800 + ps)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units in (1, 16, 256):
+        out = dc.run(num_units=units, min_chunk=32)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"ps{ps} u{units}")
