@@ -140,7 +140,8 @@ typedef struct {
   size_t workspace_bytes;
   int32_t device;
   int32_t reserved;
-  uint64_t off_counters; /* int32 [batch]: arrivals per split sequence (fused merge), left at 0 after each run */
+  uint64_t off_counters; /* int32 [batch]: arrivals per split sequence (fused merge), left at 0 after each
+                            run; then 8 int32: the split of the last attention launch, for the merge */
   uint64_t off_part_o;   /* float32 [2 * num_units * max_q_len, 16, 512]: normalised split partials */
   uint64_t off_part_lse; /* float32 [2 * num_units * max_q_len, 16]: log2-sum-exp of each partial */
 } mla_decode_plan_t;
@@ -182,8 +183,11 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
  * with MLA_FLAG_FUSED_MERGE).  mla_decode_merge enqueues the merge of those
  * partials into `out` (nothing with MLA_FLAG_FUSED_MERGE); it must follow
  * mla_decode_attend on the same stream with the same plan, qo_indptr,
- * kv_indptr and out, before the workspace is used again.  Arguments as for
- * mla_decode_run_paged, which is these two calls in order.
+ * kv_indptr and out, before the workspace is used again: it reads the split
+ * that launch chose from the workspace.  Before any mla_decode_attend on a
+ * plan's workspace it writes nothing; a sequence that does not fit the split
+ * found there (another kv_indptr) is skipped, never read out of bounds.
+ * Arguments as for mla_decode_run_paged, which is these two calls in order.
  */
 mla_status mla_decode_attend(const mla_decode_plan_t* plan, const void* q, const void* kv,
                              const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,

@@ -75,7 +75,7 @@ Layout layout_for(const mla_decode_params* p, int32_t units) {
   const size_t slots = (size_t)2 * units * max_q_of(p);
   Layout L;
   L.counters = 0;
-  L.part_o = align_up((size_t)p->batch * sizeof(int32_t));
+  L.part_o = align_up(((size_t)p->batch + mla::kGeoWords) * sizeof(int32_t));
   L.part_lse = L.part_o + align_up(slots * mla::kHeads * mla::kVDim * sizeof(float));
   L.total = L.part_lse + align_up(slots * mla::kHeads * sizeof(float));
   return L;
@@ -206,8 +206,9 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
   pl.off_part_lse = L.part_lse;
 
   int32_t* counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + L.counters);
-  const int nb = (params->batch + 255) / 256;
-  hipLaunchKernelGGL(mla::mla_fill_i32_kernel, dim3(nb), dim3(256), 0, stream, counters, params->batch, 0);
+  // arrival counters and the split record (all zero: no split recorded yet)
+  const int n = params->batch + mla::kGeoWords;
+  hipLaunchKernelGGL(mla::mla_fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, counters, n, 0);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   *plan = pl;
   return MLA_OK;

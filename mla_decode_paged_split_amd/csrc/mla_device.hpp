@@ -111,6 +111,7 @@ struct alignas(16) Smem {
   float lsum[kWaves][QL][kHeads];
   int seq[kSeqTable][4];  // kv_indptr[b], kv_indptr[b+1], qo_indptr[b], (tokens << 16) | last-page rows
                           // of the first kSeqTable sequences
+  int differs[kWaves];  // per wave: some sequence's length differs from the first's
   int bmin;
   int bmax;
   int arrive;
@@ -130,7 +131,7 @@ struct Args {
   uint16_t* out;      // bf16 bits [total_q, 16, 512]
   float* part_o;      // [2*units*max_q_len, 16, 512]
   float* part_lse;    // [2*units*max_q_len, 16], log2 domain
-  int32_t* counters;  // [batch]
+  int32_t* counters;  // [batch] arrivals, then kGeoWords words: the split of the last attention launch
   int32_t batch;
   int32_t units;
   int32_t min_chunk;  // rows
@@ -252,14 +253,17 @@ __device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w) {
 // part-filled.  C is a multiple of max(1, 32 / page_size) and at least
 // min_chunk rows' worth of pages.
 //
-// When the sequences are short on average (fewer than kCostMinAvgRows rows),
-// every sequence also carries a fixed cost of kPieceCostRows rows: sequence b
-// occupies [kv_indptr[b] - base + cost * b, ... + its positions) of a "cost
-// space" whose gaps belong to no one, and the shares cut that space.  Each
-// piece a workgroup walks has a fixed price (a ring start, the Q load, the
-// finish) of about three tiles, so without the term a share of many short
-// sequences serialises them all on one workgroup.  With long sequences the
-// cost is 0 and the space is the positions themselves.
+// Every sequence may also carry a fixed cost of kPieceCostRows rows:
+// sequence b then occupies [kv_indptr[b] - base + cost * b, ... + its
+// positions) of a "cost space" whose gaps belong to no one, and the shares
+// cut that space.  Each piece a workgroup walks has a fixed price (a ring
+// start, the Q load, the finish) of about three tiles, so without the term a
+// share that holds many sequence starts (many short sequences, or ragged
+// lengths) takes that price many times while its neighbours take it once.
+// The cost is left out (0) only where it cannot help: every sequence has the
+// same length, at least kCostMinAvgRows rows, and that length and the share
+// size divide one into the other, so every share holds whole sequences or
+// whole fractions of one.
 constexpr int kPieceCostRows = 192;
 constexpr int kCostMinAvgRows = 1024;
 
@@ -270,21 +274,44 @@ struct Geo {
   int32_t chunk;  // C positions per workgroup share
   int32_t n_wg;   // shares in use (>= 1)
 };
+constexpr int kGeoWords = 8;  // the attention launch's Geo, kept for the merge launch after the counters
 
-__device__ __forceinline__ Geo make_geo(const int32_t* kv_indptr, int batch, int units, int min_chunk, int sh) {
+// Share size: ceil(total / units) rounded up to align (a power of two), at
+// least min_pos.  Totals fit int32 (the pool rows do), so the divisions are
+// 32-bit unsigned ones.
+__device__ __forceinline__ int32_t share_size(int32_t total, int units, int align, int min_pos) {
+  const uint32_t c = ((uint32_t)total + (uint32_t)units - 1u) / (uint32_t)units;
+  const int32_t r = (int32_t)((c + (uint32_t)align - 1u) & ~((uint32_t)align - 1u));
+  return r < min_pos ? min_pos : r;
+}
+
+__device__ __forceinline__ int32_t share_count(int32_t total, int32_t chunk) {
+  const int32_t n = (int32_t)(((uint32_t)total + (uint32_t)chunk - 1u) / (uint32_t)chunk);
+  return n < 1 ? 1 : n;
+}
+
+// The split with no cost term.
+__device__ __forceinline__ Geo cost_free_geo(const int32_t* kv_indptr, int batch, int units, int min_chunk, int sh) {
   Geo g;
   g.base = kv_indptr[0];
-  const int pos = kv_indptr[batch] - g.base;
-  g.cost = ((int64_t)pos < (int64_t)batch * max(1, kCostMinAvgRows >> sh)) ? max(1, kPieceCostRows >> sh) : 0;
-  g.total = pos + g.cost * batch;
-  const int align = max(1, kSplitAlign >> sh);
-  const int min_pos = max(1, min_chunk >> sh);
-  int64_t c = ((int64_t)g.total + units - 1) / units;
-  c = (c + align - 1) / align * align;
-  if (c < min_pos) c = min_pos;
-  g.chunk = (int32_t)c;
-  int64_t n = ((int64_t)g.total + c - 1) / c;
-  g.n_wg = n < 1 ? 1 : (int32_t)n;
+  g.cost = 0;
+  g.total = kv_indptr[batch] - g.base;
+  g.chunk = share_size(g.total, units, max(1, kSplitAlign >> sh), max(1, min_chunk >> sh));
+  g.n_wg = share_count(g.total, g.chunk);
+  return g;
+}
+
+// The split: the cost-free one g0 when every sequence has the same length
+// (uniform_len >= 0; -1 if they differ), at least kCostMinAvgRows rows, that
+// divides the share size or is divided by it; else one with the cost term.
+__device__ __forceinline__ Geo make_geo(const Geo& g0, int batch, int units, int min_chunk, int sh, int uniform_len) {
+  const bool long_seqs = uniform_len >= max(1, kCostMinAvgRows >> sh);
+  if (long_seqs && (uniform_len % g0.chunk == 0 || g0.chunk % uniform_len == 0)) return g0;
+  Geo g = g0;
+  g.cost = max(1, kPieceCostRows >> sh);
+  g.total += g.cost * batch;
+  g.chunk = share_size(g.total, units, max(1, kSplitAlign >> sh), max(1, min_chunk >> sh));
+  g.n_wg = share_count(g.total, g.chunk);
   return g;
 }
 
@@ -902,9 +929,62 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   const float ks = (KT == Dt::FP8) ? *a.kv_scale : 1.0f;
   // these loads go out before the ring's, so using them never waits for the ring's indices
   __builtin_amdgcn_sched_barrier(0);
-  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, sh);
+
+  // The first round trip's values go to the LDS sequence table before the
+  // ring's indices are requested, so no register waiting on them stays live
+  // while the indices are in flight (the compiler's wait counts would
+  // otherwise drain the indices at the first join).  The same pass finds
+  // whether every sequence is as long as the first, which the split needs (a
+  // ballot per wave, so no shuffle chain).
+  // Every entry is written, past the batch too (with the clamped values;
+  // nothing reads those): a load consumed on one path only would make the
+  // compiler wait for all loads, the ring's included, where the paths join.
+  const int len0 = a.kv_indptr[1] - a.kv_indptr[0];
+  bool differs = false;
+#pragma unroll
+  for (int i = 0; i < kScanPerThread; ++i) {
+    const int j = threadIdx.x + i * kThreads;
+    sm.seq[j][0] = sv[i][0];
+    sm.seq[j][1] = sv[i][1];
+    sm.seq[j][2] = sv[i][2];
+    sm.seq[j][3] = pack_seq_aux(a, sv[i][2], sv[i][3], sv[i][4], paged);
+    differs |= (j < a.batch) & (sv[i][1] - sv[i][0] != len0);
+  }
+  if constexpr (kBigBatch) {
+    for (int j = threadIdx.x + kSeqTable; j < a.batch; j += kThreads)
+      differs |= a.kv_indptr[j + 1] - a.kv_indptr[j] != len0;
+  }
+  const bool wave_differs = __ballot(differs) != 0;
+  if ((threadIdx.x & 63) == 0) sm.differs[threadIdx.x >> 6] = wave_differs ? 1 : 0;
+  if (threadIdx.x == 0) {
+    sm.bmin = 0x7fffffff;
+    sm.bmax = -1;
+  }
+
+  // The split is known only after the barrier below, but the cost-free one
+  // (the usual one for uniform lengths) is known now, and under it the first
+  // piece always starts at the share start (the sequence holding position lo
+  // begins at or before it).  So the page indices of that piece's ring are
+  // fetched now, clamped to the share's pages, while the barrier and the scan
+  // below run; the piece issues the rows once its Q is on the way.  If the
+  // split turns out to carry the cost, the pieces fetch their own.
   const int k = blockIdx.x;
+  Ring<KT, ring_depth<QT, KT, QL>()> ring;
+  const Geo g0 = cost_free_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, sh);
+  {
+    const int lo0 = k * g0.chunk;
+    if (lo0 < g0.total) {  // a share with positions: its indices exist
+      issue_ring_indices(a.kv_indices, g0.base + lo0, (min(lo0 + g0.chunk, g0.total) - lo0) << sh, sh, ring);
+    }
+  }
+  __syncthreads();  // the table, the length flags and bmin / bmax are in place
+  const bool uniform = (sm.differs[0] | sm.differs[1] | sm.differs[2] | sm.differs[3]) == 0;
+  const Geo geo = make_geo(g0, a.batch, a.units, a.min_chunk, sh, uniform ? len0 : -1);
   if (k >= geo.n_wg) return;
+  if (k == 0 && threadIdx.x < 5) {  // the split, for the merge launch
+    const int32_t v[5] = {geo.base, geo.cost, geo.total, geo.chunk, geo.n_wg};
+    a.counters[a.batch + threadIdx.x] = v[threadIdx.x];
+  }
   const int lo = k * geo.chunk;
   const int hi = min(lo + geo.chunk, geo.total);
 
@@ -916,35 +996,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   logit.k2 = a.logit_cap * kLog2e;
   const float out_mul = ks;
 
-  // Without the per-sequence cost the first piece always starts at the share
-  // start (the sequence holding position lo begins at or before it), so the
-  // page indices of its ring can be fetched now, clamped to the share's
-  // pages, while the scan below finds the sequences; the piece issues the
-  // rows once its Q is on the way.  With the cost the share may start in a gap.
-  const bool primed = geo.cost == 0;
-  Ring<KT, ring_depth<QT, KT, QL>()> ring;
-
-  // The first round trip's values go to the LDS sequence table before the
-  // ring's indices are requested, so no register waiting on them stays live
-  // while the indices are in flight (the compiler's wait counts would
-  // otherwise drain the indices at the first join).
-#pragma unroll
-  for (int i = 0; i < kScanPerThread; ++i) {
-    const int j = threadIdx.x + i * kThreads;
-    if (j < a.batch) {
-      sm.seq[j][0] = sv[i][0];
-      sm.seq[j][1] = sv[i][1];
-      sm.seq[j][2] = sv[i][2];
-      sm.seq[j][3] = pack_seq_aux(a, sv[i][2], sv[i][3], sv[i][4], paged);
-    }
-  }
-  if (threadIdx.x == 0) {
-    sm.bmin = 0x7fffffff;
-    sm.bmax = -1;
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if (primed) issue_ring_indices(a.kv_indices, geo.base + lo, (hi - lo) << sh, sh, ring);
-  __syncthreads();  // the table and bmin / bmax are in place
+  const bool primed = geo.cost == 0;  // the ring's indices above are the first piece's
   // (empty sequences are zeroed after the pieces: stores here would enter the
   // compiler's count of loads in flight and make the prologue wait for all)
   auto scan_one = [&](int j, int ipb, int ipe) {
@@ -1066,10 +1118,20 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int b = blockIdx.x;
   const int h = blockIdx.y;
   const int tau = blockIdx.z;
-  const Geo geo = make_geo(a.kv_indptr, a.batch, a.units, a.min_chunk, a.page_shift);
+  const int32_t* gr = a.counters + a.batch;  // the split the attention launch used
+  Geo geo;
+  geo.base = gr[0];
+  geo.cost = gr[1];
+  geo.total = gr[2];
+  geo.chunk = gr[3];
+  geo.n_wg = gr[4];
   const int st = a.kv_indptr[b] - geo.base + geo.cost * b;
   const int en = st + (a.kv_indptr[b + 1] - a.kv_indptr[b]);
   if (en <= st) return;
+  // A split that does not hold this sequence (none recorded yet: chunk 0, or
+  // another kv_indptr) is skipped: every slot read below is then < 2 * n_wg
+  // <= 2 * units, inside the partial buffers.
+  if (geo.chunk < 1 || geo.n_wg > a.units || st < 0 || en > geo.total || (en - 1) / geo.chunk >= geo.n_wg) return;
   const int qo = a.qo_indptr[b];
   if (a.max_q_len > 1) {
     const int q_len = min(max(a.qo_indptr[b + 1] - qo, 0), a.max_q_len);

@@ -58,12 +58,13 @@ def _params(**kw):
 def test_workspace_size_is_host_arithmetic():
     p = _params(batch=64, num_units=256)
     n = B.mla_decode_workspace_size(p)
-    # counters (64 int32, padded to 256 B) + partial O (2*256*16*512 fp32) + partial lse (2*256*16 fp32)
-    assert n == 256 + 2 * 256 * 16 * 512 * 4 + 2 * 256 * 16 * 4
+    # counters (64 int32 + 8 int32 of split record, padded to 256 B) + partial O (2*256*16*512 fp32)
+    # + partial lse (2*256*16 fp32)
+    assert n == 512 + 2 * 256 * 16 * 512 * 4 + 2 * 256 * 16 * 4
     assert B.mla_decode_workspace_size(_params(batch=1000, num_units=4)) == 4096 + 2 * 4 * 16 * 512 * 4 + 512
     # with several query tokens every partial slot has a row per token
     assert B.mla_decode_workspace_size(_params(batch=64, total_q=128, num_units=256, max_q_len=2)) == \
-        256 + 2 * 2 * 256 * 16 * 512 * 4 + 2 * 2 * 256 * 16 * 4
+        512 + 2 * 2 * 256 * 16 * 512 * 4 + 2 * 2 * 256 * 16 * 4
 
 
 @pytest.mark.parametrize(

@@ -307,15 +307,90 @@ def test_batch_beyond_lds_table(gpu, qd, kd):
         out = dc.run(num_units=units, min_chunk=32)
         torch.cuda.synchronize()
         assert_parity(ref, to64(out), f"big batch short {qd}/{kd} u{units}")
-    long_ = rng.integers(1024, 1400, size=1030).tolist()  # without it
-    spec = synth.CaseSpec(batch=1030, q_dtype=qd, kv_dtype=kd, lengths=long_, permuted=True, seed=3301)
+    # equal lengths of 1024 rows and shares of 2048 (515 units): without the cost; then the same with one
+    # length changed past the LDS table, which only the scan from memory sees: with it
+    seqs = [0, 1, 513, 1023, 1024, 1025, 1027, 1029]
+    for lens, cost in (([1024] * 1030, 0), ([1024] * 1027 + [1023] + [1024] * 2, 192)):
+        spec = synth.CaseSpec(batch=1030, q_dtype=qd, kv_dtype=kd, lengths=lens, permuted=True, seed=3301)
+        case = synth.make_case(spec)
+        dc = DevCase(case, gpu)
+        dec = dc.decoder(num_units=515, min_chunk=32)
+        out = dc.run(dec)
+        torch.cuda.synchronize()
+        assert split_record(dec)[1] == cost
+        assert split_record(dec) == expected_split(case, 515, 32)
+        ref = oracle_ref(case, sequences=seqs)
+        assert_parity(ref[seqs], to64(out)[seqs], f"big batch long {qd}/{kd} cost {cost}")
+        del dc, case
+
+
+def split_record(dec: binding.Decoder) -> list:
+    """The split (base, cost, total, chunk, shares) the last attention launch recorded in the workspace."""
+    words = dec.workspace.view(torch.int32)
+    at = dec.plan.off_counters // 4 + dec.params.batch
+    return words[at:at + 5].cpu().tolist()
+
+
+def expected_split(case, units: int, min_chunk: int) -> list:
+    """The split rule restated on the host: positions are pages; every sequence costs 192 rows of
+    positions unless all have one length of at least 1024 rows that the share size divides or is
+    divided by."""
+    sh = case.spec.page_size.bit_length() - 1
+    ind = case.kv_indptr.tolist()
+    lens = [ind[i + 1] - ind[i] for i in range(len(ind) - 1)]
+    pos = ind[-1] - ind[0]
+
+    def share(total):
+        c = -(-total // units)
+        al = max(1, 32 >> sh)
+        return max(-(-c // al) * al, max(1, min_chunk >> sh))
+
+    c0 = share(pos)
+    L = lens[0]
+    if all(x == L for x in lens) and L >= max(1, 1024 >> sh) and (L % c0 == 0 or c0 % L == 0):
+        cost, total, chunk = 0, pos, c0
+    else:
+        cost = max(1, 192 >> sh)
+        total = pos + cost * len(lens)
+        chunk = share(total)
+    return [ind[0], cost, total, chunk, max(1, -(-total // chunk))]
+
+
+@pytest.mark.parametrize("lens,page,units,cost", [
+    ([4096] * 8, 1, 256, 0),  # equal, long, shares of 128 divide the length
+    ([5000] * 3, 1, 256, 192),  # equal and long, but shares of 64 neither divide nor are divided by 5000
+    ([512] * 16, 1, 256, 192),  # equal but short
+    ([8192, 8191, 8192, 8192], 1, 64, 192),  # one length differs
+    ([8010] * 4, 16, 256, 12),  # pages of 16: 501 positions each, shares of 16 positions; cost 192 >> 4
+    ([8192] * 64, 16, 256, 0),  # pages of 16, shares of 128 positions
+])
+def test_split_rule(gpu, lens, page, units, cost):
+    spec = synth.CaseSpec(batch=len(lens), q_dtype="bf16", kv_dtype="fp8", lengths=lens, page_size=page,
+                          seed=3350 + len(lens))
     case = synth.make_case(spec)
     dc = DevCase(case, gpu)
-    out = dc.run()
+    dec = dc.decoder(num_units=units)
+    out = dc.run(dec)
     torch.cuda.synchronize()
-    seqs = [0, 1, 513, 1023, 1024, 1025, 1029]
+    rec = split_record(dec)
+    log(f"  split {rec} for {len(lens)} sequences, pages of {page}, {units} units")
+    assert rec[1] == cost
+    assert rec == expected_split(case, units, dec.plan.params.min_chunk)
+    seqs = list(range(min(len(lens), 4)))
     ref = oracle_ref(case, sequences=seqs)
-    assert_parity(ref[seqs], to64(out)[seqs], f"big batch long {qd}/{kd}")
+    assert_parity(ref[seqs], to64(out)[seqs], f"split rule {lens[:2]} p{page} u{units}")
+
+
+def test_merge_before_any_attention_writes_nothing(gpu):
+    spec = synth.CaseSpec(batch=4, q_dtype="bf16", kv_dtype="fp8", lengths=[3000, 10, 4000, 700], seed=3360)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    dec = dc.decoder(num_units=64)
+    out = torch.full((4, 16, 512), float("nan"), dtype=torch.bfloat16, device=gpu)
+    binding.mla_decode_merge(dec.plan, dc.qo_indptr, dc.kv_indptr, out)
+    torch.cuda.synchronize()
+    assert split_record(dec) == [0, 0, 0, 0, 0]
+    assert bool(torch.isnan(out.float()).all())
 
 
 def test_batch_beyond_lds_table_with_tokens(gpu):
