@@ -555,10 +555,15 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     for (int q = 0; q < QL; ++q) {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) +
                            (size_t)(pc.t0 + (q < pc.ntok ? q : 0)) * kHeads * kQKDim * (src16 ? 2 : 1);
+      // every thread issues all kPer loads (index clamped; surplus ones are not
+      // written to LDS): the compiler counts only unconditional loads when it
+      // works out how long the ring's row addresses must wait for their page
+      // indices, and a load inside a branch would make the third tile's rows
+      // wait for the first Q load
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-        if (c < nchunks) stage[q][i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)c * 16);
+        const int c = min((int)threadIdx.x + i * kThreads, nchunks - 1);
+        stage[q][i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)c * 16);
       }
     }
     issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
