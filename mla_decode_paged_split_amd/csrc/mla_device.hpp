@@ -622,11 +622,10 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   auto& dat = ring.dat;
   auto& idxn = ring.next;
   auto page_index = [&](int tt) { return piece_page(a.kv_indices, pc.ip0, pc.nrows, tt * kTileRows + my_row, sh); };
-  auto load_tile = [&](u32x4_t(&dst)[L::kChunks], int page, int tt) {
+  // this lane's first 16-byte chunk of its row of tile tt (the row's chunks j are 64 bytes apart)
+  auto tile_src = [&](int page, int tt) {
     const int row = page_row(page, pc.nrows, tt * kTileRows + my_row, sh);
-    const uint8_t* src = kvb + (size_t)row * L::kRowBytes + g * 16;
-#pragma unroll
-    for (int j = 0; j < L::kChunks; ++j) dst[j] = *reinterpret_cast<const u32x4_t*>(src + j * 64);
+    return kvb + (size_t)row * L::kRowBytes + g * 16;
   };
 
   float m_run[QL];
@@ -731,6 +730,19 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       s1[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     uint8_t* vrow = &sm.v[buf][16 * w + c16][0];
+    // The slot is refilled with tile tt + D chunk by chunk, each load issued
+    // right after its chunk is used (rows past the piece clamp to its first
+    // row, so every steady-state trip issues the same loads and the compiler's
+    // wait counts stay exact).  Spread over the products, the four waves' loads
+    // reach the address unit a few at a time instead of as one burst of 36 that
+    // would hold each wave for most of a tile.
+    // The index of tile tt + 2D goes out before these refills, so the next
+    // use of the slot waits for it without waiting for all of its tile.
+    const uint8_t* nsrc = nullptr;
+    if constexpr (decltype(refill)::value) {
+      nsrc = tile_src(idxn[k], tt + D);
+      idxn[k] = page_index(tt + 2 * D);
+    }
 #pragma unroll
     for (int j = 0; j < L::kChunks; ++j) {
       const u32x4_t kk = dat[k][j];
@@ -761,14 +773,11 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
           s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k1, (long)q8[q][2 * j + 1], s1[q], 0, 0, 0);
         }
       }
-    }
-    // ---- refill this ring slot with tile tt + D, fetch the index of tile tt + 2D.
-    // Issued unconditionally in the steady-state loop (rows past the piece
-    // clamp to its first row), so every trip issues the same loads and the
-    // compiler's wait counts stay exact: the ring really keeps D tiles in flight.
-    if constexpr (decltype(refill)::value) {
-      load_tile(dat[k], idxn[k], tt + D);
-      idxn[k] = page_index(tt + 2 * D);
+      if constexpr (decltype(refill)::value) {
+        __builtin_amdgcn_sched_barrier(0);
+        dat[k][j] = *reinterpret_cast<const u32x4_t*>(nsrc + j * 64);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // ---- previous tile's P.V (its weights and V were published before the last barrier)
     if (tt > 0) pv(tt - 1);
