@@ -144,13 +144,54 @@ struct Args {
 
 // ------------------------------------------------------------------ helpers
 
+// Max / sum of x over lanes l and l ^ 16 (l ^ 32) of the wave, on the VALU:
+// v_permlane16_swap / v_permlane32_swap of x with a copy of itself hands
+// every lane the pair's two values (lower lane's first), where a shuffle
+// would go through the LDS unit and cost a round trip there.  Written as one
+// asm block: through the compiler builtin, given the same value twice, the
+// swap's two results were folded into one and each lane combined its own
+// value with itself.  The s_nop pairs cover the VALU-write-then-permlane
+// hazard, which the compiler cannot see inside the block.
+template <bool k32>
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  a = x;
+  if constexpr (k32)
+    asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "=&v"(b));
+  else
+    asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "=&v"(b));
+}
+__device__ __forceinline__ float pair_max16(float x) {
+  float a, b;
+  lane_pair<false>(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  float a, b;
+  lane_pair<true>(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  float a, b;
+  lane_pair<false>(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  float a, b;
+  lane_pair<true>(x, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  v = pair_max32(v);
+  v = pair_max16(v);
+  for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v = pair_sum32(v);
+  v = pair_sum16(v);
+  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
 
@@ -795,8 +836,8 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         x[q][i] = (pr < pc.lim[q]) ? y[i] : -INFINITY;
         mx = fmaxf(mx, x[q][i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair_max16(mx);
+      mx = pair_max32(mx);
       if (g == 0) sm.mx[buf][w][q][c16] = mx;
     }
     // ---- speculative weights with the running max known so far
@@ -865,8 +906,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // ---- finish: per-head row sums of the 4 waves, then this wave's 128 columns
 #pragma unroll
   for (int q = 0; q < QL; ++q) {
-    float l_tot = l_run[q] + __shfl_xor(l_run[q], 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = pair_sum32(pair_sum16(l_run[q]));
     if (g == 0) sm.lsum[w][q][c16] = l_tot;
   }
   __syncthreads();
