@@ -117,7 +117,7 @@ typedef struct {
   int32_t num_units;    /* 0 = the device's compute-unit count.  Upper bound on the
                            workgroups that split the KV rows; each one owns a
                            contiguous share of all sequences' rows. */
-  int32_t min_chunk;    /* 0 = default (256).  Smallest share of KV rows per workgroup;
+  int32_t min_chunk;    /* 0 = default (64).  Smallest share of KV rows per workgroup;
                            must be a multiple of 32 when set. */
   uint32_t flags;       /* MLA_FLAG_* */
   int32_t max_q_len;    /* 0 = 1.  Most query tokens of one sequence (qo_indptr[b+1] -

@@ -15,7 +15,11 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kDefaultMinChunk = 256;
+// Smallest share by default: one 64-row tile.  Small batches then spread
+// over more workgroups with fewer tiles each (4 sequences of 1024 rows: 64
+// workgroups of one tile instead of 16 of four, 13 us instead of 19); below
+// this the merge of many pieces costs more than it saves.
+constexpr int kDefaultMinChunk = 64;
 constexpr int kMaxPageSize = 1024;
 constexpr int kMaxQLen = 16;
 constexpr uint32_t kKnownFlags = MLA_FLAG_FUSED_MERGE | MLA_FLAG_FUSED_Q_CAST | MLA_FLAG_CAUSAL;
