@@ -160,6 +160,43 @@ __device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
   else
     asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "=&v"(b));
 }
+// The same exchange for two independent values in one block, so the two
+// chains overlap (separate volatile blocks keep their order and run back to
+// back).
+template <bool k32>
+__device__ __forceinline__ void lane_pair2(float x0, float x1, float& a0, float& b0, float& a1, float& b1) {
+  a0 = x0;
+  a1 = x1;
+  if constexpr (k32)
+    asm volatile(
+        "v_mov_b32 %1, %0\n\tv_mov_b32 %3, %2\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\t"
+        "v_permlane32_swap_b32 %2, %3\n\ts_nop 1"
+        : "+v"(a0), "=&v"(b0), "+v"(a1), "=&v"(b1));
+  else
+    asm volatile(
+        "v_mov_b32 %1, %0\n\tv_mov_b32 %3, %2\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\t"
+        "v_permlane16_swap_b32 %2, %3\n\ts_nop 1"
+        : "+v"(a0), "=&v"(b0), "+v"(a1), "=&v"(b1));
+}
+
+// Max of x[q] over the four lanes l, l ^ 16, l ^ 32, l ^ 48, for each of N values.
+template <int N>
+__device__ __forceinline__ void quad_max(float (&x)[N]) {
+  static_assert(N == 1 || N == 2, "one or two values");
+  if constexpr (N == 1) {
+    float a, b;
+    lane_pair<false>(x[0], a, b);
+    lane_pair<true>(fmaxf(a, b), a, b);
+    x[0] = fmaxf(a, b);
+  } else {
+    float a0, b0, a1, b1;
+    lane_pair2<false>(x[0], x[1], a0, b0, a1, b1);
+    lane_pair2<true>(fmaxf(a0, b0), fmaxf(a1, b1), a0, b0, a1, b1);
+    x[0] = fmaxf(a0, b0);
+    x[1] = fmaxf(a1, b1);
+  }
+}
+
 __device__ __forceinline__ float pair_max16(float x) {
   float a, b;
   lane_pair<false>(x, a, b);
@@ -302,11 +339,11 @@ __device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w) {
 // share that holds many sequence starts (many short sequences, or ragged
 // lengths) takes that price many times while its neighbours take it once.
 // The cost is left out (0) only where it cannot help: every sequence has the
-// same length, at least kCostMinAvgRows rows, and that length and the share
+// same length, at least kCostFreeMinRows rows, and that length and the share
 // size divide one into the other, so every share holds whole sequences or
 // whole fractions of one.
 constexpr int kPieceCostRows = 192;
-constexpr int kCostMinAvgRows = 1024;
+constexpr int kCostFreeMinRows = 1024;
 
 struct Geo {
   int32_t base;   // kv_indptr[0]
@@ -343,10 +380,10 @@ __device__ __forceinline__ Geo cost_free_geo(const int32_t* kv_indptr, int batch
 }
 
 // The split: the cost-free one g0 when every sequence has the same length
-// (uniform_len >= 0; -1 if they differ), at least kCostMinAvgRows rows, that
+// (uniform_len >= 0; -1 if they differ), at least kCostFreeMinRows rows, that
 // divides the share size or is divided by it; else one with the cost term.
 __device__ __forceinline__ Geo make_geo(const Geo& g0, int batch, int units, int min_chunk, int sh, int uniform_len) {
-  const bool long_seqs = uniform_len >= max(1, kCostMinAvgRows >> sh);
+  const bool long_seqs = uniform_len >= max(1, kCostFreeMinRows >> sh);
   if (long_seqs && (uniform_len % g0.chunk == 0 || g0.chunk % uniform_len == 0)) return g0;
   Geo g = g0;
   g.cost = max(1, kPieceCostRows >> sh);
@@ -824,22 +861,24 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     if (tt > 0) pv(tt - 1);
     // ---- scores (log2 domain), masked past the rows each token sees
     float x[QL][4];
+    float mx[QL];
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
       const f32x4_t sc = s0[q] + s1[q];
       float y[4];
       logit.apply<kGeneral>(sc, y);
-      float mx = -INFINITY;
+      mx[q] = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pr = tt * kTileRows + 16 * w + g * 4 + i;
         x[q][i] = (pr < pc.lim[q]) ? y[i] : -INFINITY;
-        mx = fmaxf(mx, x[q][i]);
+        mx[q] = fmaxf(mx[q], x[q][i]);
       }
-      mx = pair_max16(mx);
-      mx = pair_max32(mx);
-      if (g == 0) sm.mx[buf][w][q][c16] = mx;
     }
+    quad_max<QL>(mx);  // over the wave's 16 rows of each head
+#pragma unroll
+    for (int q = 0; q < QL; ++q)
+      if (g == 0) sm.mx[buf][w][q][c16] = mx[q];
     // ---- speculative weights with the running max known so far
     u32x2_t pw[QL];
     auto make_p = [&]() {
