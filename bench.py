@@ -100,8 +100,25 @@ def load_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, opts, budget_s: float):
-    """Time the float64 oracle on whole sequences until about budget_s of CPU work."""
+def cpu_baseline(case, opts, budget_s: float, single_thread_s: float = 0.0):
+    """Time the float64 oracle on whole sequences until about budget_s of CPU work (all host threads the
+    numeric library uses), then, if single_thread_s > 0, again with one thread for about that long."""
+    import oracle
+
+    res = _cpu_oracle_rate(case, opts, budget_s)
+    if single_thread_s > 0:
+        try:
+            from threadpoolctl import threadpool_limits
+
+            with threadpool_limits(limits=1):
+                one = _cpu_oracle_rate(case, opts, single_thread_s)
+            res["single_thread"] = {"value": one["value"], "unit": "GB/s", "cores": 1, "sample": one["sample"]}
+        except ImportError:  # pragma: no cover
+            pass
+    return res
+
+
+def _cpu_oracle_rate(case, opts, budget_s: float):
     import oracle
 
     try:
@@ -169,6 +186,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-budget-single", type=float, default=4.0,
+                    help="seconds of oracle work with one host thread (0: skip)")
     ap.add_argument("--rotate-bytes", type=float, default=2**30, help="KV bytes to rotate through (cache defeat)")
     ap.add_argument("--num-units", type=int, default=0)
     ap.add_argument("--min-chunk", type=int, default=0)
@@ -275,6 +294,35 @@ def main() -> int:
     kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     kern_med_ms = kern_ms[len(kern_ms) // 2]
+    kern_p10_ms = kern_ms[len(kern_ms) // 10]
+    kern_p90_ms = kern_ms[(len(kern_ms) * 9) // 10]
+
+    # diagnostics (not the contract figures): the attention launch with one KV copy reused (rows warm in
+    # the last-level cache where they fit), the plan call, and a plain streaming read on the same device
+    n_diag = min(args.steps, 50)
+    for i in range(n_diag):
+        step(0, evs[i])
+    torch.cuda.synchronize()
+    hot_ms = sorted(a.elapsed_time(b) for a, b in evs[:n_diag])
+    hot_med_ms = hot_ms[len(hot_ms) // 2]
+    torch.cuda.synchronize()
+    plan_t0 = time.perf_counter()
+    for _ in range(20):
+        binding.mla_decode_plan(dec.params, dec.workspace, stream)
+    torch.cuda.synchronize()
+    plan_us = (time.perf_counter() - plan_t0) / 20 * 1e6
+    probe = torch.ones(1 << 30, dtype=torch.uint8, device=dev)  # 1 GiB
+    sink = torch.empty(binding.MLA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        binding.mla_read_probe(probe, sink, stream)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(10):
+        binding.mla_read_probe(probe, sink, stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    probe_gbs = probe.numel() * 10 / (t_start.elapsed_time(t_end) * 1e-3) / 1e9
+    del probe, sink
 
     q_elt = 1 if sep_cast else 2  # the attention launch reads fp8 Q, or bf16 Q it casts itself
     alg_bytes = algorithmic_bytes(spec, case, q_elt)
@@ -336,6 +384,8 @@ def main() -> int:
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
             "kernel_median_us": round(kern_med_ms * 1e3, 2),
+            "kernel_p10_us": round(kern_p10_ms * 1e3, 2),
+            "kernel_p90_us": round(kern_p90_ms * 1e3, 2),
             "mfma": {
                 "flops_per_launch": flops,
                 "achieved_tflops": round(mfma_tflops, 1),
@@ -344,11 +394,20 @@ def main() -> int:
                 "frac": round(mfma_tflops / PEAK_MFMA_TFLOPS[mfma_dtype], 4),
             },
         },
+        "diagnostics": {
+            "attention_median_us_one_kv_copy_reused": round(hot_med_ms * 1e3, 2),
+            "plan_us_per_call_host": round(plan_us, 1),
+            "read_probe": {
+                "kind": "mla_read_probe: 16-byte streaming reads of 1 GiB, 1024 workgroups x 256 threads, same device",
+                "GBps": round(probe_gbs, 1),
+                "attention_frac_of_probe": round(achieved / probe_gbs, 4),
+            },
+        },
         "wall_s_timed": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, opts, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(case, opts, args.cpu_budget, args.cpu_budget_single)
     print(json.dumps(res), flush=True)
     return 0
 

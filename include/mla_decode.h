@@ -247,6 +247,19 @@ mla_status mla_decode_quantize_q_dynamic(const void* q_bf16, void* q_fp8, float*
 mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const int32_t* part_indptr,
                              int32_t batch, void* out, hipStream_t stream);
 
+/*
+ * Diagnostic, not part of the decode path: read `bytes` of device memory at
+ * `buf` once, with 16-byte loads from 1024 workgroups of 256 threads, and
+ * store one 32-bit word per workgroup to `sink` (the xor of the words it
+ * read).  Timed around its launch, this gives the device's practical
+ * streaming read rate, beside which the decode kernels' bandwidth can be set.
+ * `buf` must be 16-byte aligned and `bytes` a positive multiple of 16; `sink`
+ * must hold at least MLA_READ_PROBE_SINK_WORDS words.  Otherwise
+ * MLA_ERR_INVALID_ARG, before any launch.
+ */
+#define MLA_READ_PROBE_SINK_WORDS 1024
+mla_status mla_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status status);
 

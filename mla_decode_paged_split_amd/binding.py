@@ -31,6 +31,8 @@ __all__ = [
     "lib",
     "mla_status_string",
     "mla_decode_abi_version",
+    "mla_read_probe",
+    "MLA_READ_PROBE_SINK_WORDS",
     "mla_decode_workspace_size",
     "mla_decode_plan",
     "mla_decode_run",
@@ -112,6 +114,8 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_decode_abi_version.argtypes = []
         L.mla_decode_abi_version.restype = i32
+        L.mla_read_probe.argtypes = [vp, sz, vp, sz, vp]
+        L.mla_read_probe.restype = ctypes.c_int
         L.mla_decode_workspace_size.argtypes = [ctypes.POINTER(MlaDecodeParams)]
         L.mla_decode_workspace_size.restype = sz
         L.mla_decode_plan.argtypes = [ctypes.POINTER(MlaDecodeParams), vp, sz, vp, ctypes.POINTER(MlaDecodePlan)]
@@ -172,6 +176,17 @@ def mla_status_string(code: int) -> str:
 
 def mla_decode_abi_version() -> int:
     return int(lib().mla_decode_abi_version())
+
+
+MLA_READ_PROBE_SINK_WORDS = 1024
+
+
+def mla_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Diagnostic streaming read of all of `buf` (see the header); `sink` holds one int32 per probe workgroup."""
+    if sink.dtype != torch.int32 or sink.numel() < MLA_READ_PROBE_SINK_WORDS:
+        raise ValueError(f"sink must be int32 with at least {MLA_READ_PROBE_SINK_WORDS} elements")
+    code = lib().mla_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(), _stream(stream))
+    _check(code, "mla_read_probe")
 
 
 def make_params(batch: int, q_dtype: str, kv_dtype: str, *, total_q: Optional[int] = None, num_units: int = 0,

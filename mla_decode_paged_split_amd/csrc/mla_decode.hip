@@ -171,6 +171,16 @@ const char* mla_status_string(mla_status status) {
 
 int32_t mla_decode_abi_version(void) { return MLA_DECODE_ABI_VERSION; }
 
+mla_status mla_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream) {
+  static_assert(mla::kProbeBlocks == MLA_READ_PROBE_SINK_WORDS, "one sink word per probe workgroup");
+  if (buf == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || sink_words < (size_t)MLA_READ_PROBE_SINK_WORDS)
+    return MLA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(mla::mla_read_probe_kernel, dim3(mla::kProbeBlocks), dim3(256), 0, stream,
+                     static_cast<const mla::u32x4_t*>(buf), (int64_t)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 size_t mla_decode_workspace_size(const mla_decode_params* params) {
   if (validate_params(params) != MLA_OK) return 0;
   int32_t units = params->num_units;

@@ -1251,6 +1251,34 @@ __global__ __launch_bounds__(64) void mla_reduce_external_kernel(const float* pa
                   out + ((size_t)b * kHeads + h) * kVDim);
 }
 
+// Streaming read probe (a diagnostic): workgroup k reads its own contiguous
+// share [k * per, (k + 1) * per) of the 16-byte words, four loads in flight per
+// thread (a grid-wide stride would put every workgroup in one narrow moving
+// window of addresses, which camps on memory channels); the words past the
+// last whole share go to the first threads of the grid.  Each workgroup stores
+// the xor of what it read so that no load can be dropped.
+constexpr int kProbeBlocks = 1024;
+__global__ __launch_bounds__(256) void mla_read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16,
+                                                             uint32_t* __restrict__ sink) {
+  __shared__ uint32_t red;
+  const int64_t per = n16 / gridDim.x;
+  const u32x4_t* share = p + (int64_t)blockIdx.x * per;
+  int64_t i = threadIdx.x;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * 256 < per; i += 4 * 256) {
+    const u32x4_t a = share[i], b = share[i + 256], c = share[i + 512], d = share[i + 768];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < per; i += 256) acc ^= share[i];
+  const int64_t tail = (int64_t)gridDim.x * per + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tail < n16) acc ^= p[tail];
+  if (threadIdx.x == 0) red = 0u;
+  __syncthreads();
+  atomicXor(&red, acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red;
+}
+
 __global__ void mla_fill_i32_kernel(int32_t* p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
