@@ -311,6 +311,24 @@ def main() -> int:
         binding.mla_decode_plan(dec.params, dec.workspace, stream)
     torch.cuda.synchronize()
     plan_us = (time.perf_counter() - plan_t0) / 20 * 1e6
+    cast_us = None
+    if fp8_q:  # step a0 on its own: the unit-scale cast and the amax-scaled one (two launches)
+        q8 = torch.empty(q_bf16.shape, dtype=torch.uint8, device=dev)
+        qs_tmp = torch.ones(1, dtype=torch.float32, device=dev)
+        cast_us = {}
+        for label, fn in (("unit_scale_one_launch", lambda: binding.mla_decode_quantize_q(q_bf16, q8, stream)),
+                          ("amax_scaled_two_launches", lambda: binding.mla_decode_quantize_q_dynamic(q_bf16, q8, qs_tmp, scratch,
+                                                                                        stream))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            t_start.record(stream)
+            for _ in range(n_diag):
+                fn()
+            t_end.record(stream)
+            torch.cuda.synchronize()
+            cast_us[label] = round(t_start.elapsed_time(t_end) / n_diag * 1e3, 2)
+        del q8, qs_tmp
     probe = torch.ones(1 << 30, dtype=torch.uint8, device=dev)  # 1 GiB
     sink = torch.empty(binding.MLA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
     for _ in range(3):
@@ -397,6 +415,7 @@ def main() -> int:
         "diagnostics": {
             "attention_median_us_one_kv_copy_reused": round(hot_med_ms * 1e3, 2),
             "plan_us_per_call_host": round(plan_us, 1),
+            "q_cast_us": cast_us,
             "read_probe": {
                 "kind": "mla_read_probe: 16-byte streaming reads of 1 GiB, 1024 workgroups x 256 threads, same device",
                 "GBps": round(probe_gbs, 1),
