@@ -102,6 +102,13 @@ constexpr int q_stage_rows() {
   return KV == Dt::FP8 ? QL * kHeads : 1;
 }
 
+// Output staging at the finish, per wave and token, inside the V buffers: 16
+// head rows of the wave's 128 columns, float32 (512 bytes) or bf16 (256
+// bytes), each row padded by 16 bytes so that rows land on different banks.
+constexpr int kOutPitchF32 = kColsPerWave * 4 + 16;
+constexpr int kOutPitchBf16 = kColsPerWave * 2 + 16;
+constexpr int kOutStageBytes = kHeads * kOutPitchF32;
+
 template <Dt KV, int QL>
 struct alignas(16) Smem {
   uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];  // V part of the current / next tile
@@ -116,6 +123,8 @@ struct alignas(16) Smem {
   int bmax;
   int arrive;
 };
+static_assert(sizeof(((Smem<Dt::FP8, 1>*)nullptr)->v) >= (size_t)kWaves * kOutStageBytes, "output staging fits the V buffers");
+static_assert(sizeof(((Smem<Dt::BF16, 1>*)nullptr)->v) >= (size_t)kWaves * kOutStageBytes, "output staging fits the V buffers");
 
 struct Args {
   const void* q;
@@ -949,32 +958,81 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     if (g == 0) sm.lsum[w][q][c16] = l_tot;
   }
   __syncthreads();
+  // Lane (c16, g) holds, for block jb and i < 4, head c16 at column
+  // 128w + (4g+i)*8 + jb: a contiguous run of 32 columns.  Written straight
+  // from there, every store instruction puts 16 bytes into each of 64
+  // different lines.  With one token per pass each wave stages its rows in LDS
+  // instead (the V buffers are free once the last P.V is done) and reads them
+  // back so that every store covers whole runs of the wave's 128 columns of 2
+  // heads (float32) or 4 heads (bf16); reads follow the same wave's writes in
+  // issue order.  Two-token passes have no registers to spare and store
+  // directly.
+  uint8_t* const stage = &sm.v[0][0][0] + (size_t)w * kOutStageBytes;
 #pragma unroll
   for (int q = 0; q < QL; ++q) {
     if (q >= pc.ntok) break;  // uniform
     const float Lsum = sm.lsum[0][q][c16] + sm.lsum[1][q][c16] + sm.lsum[2][q][c16] + sm.lsum[3][q][c16];
     const float scale = Lsum > 0.f ? out_mul / Lsum : 0.f;
     const int t = pc.t0 + q;
-    // lane (c16, g) holds, for block jb and i < 4, head c16 at column 128w + (4g+i)*8 + jb
+    if constexpr (QL > 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = kColsPerWave * w + (4 * g + i) * 8;
-      if (pc.complete) {
+      for (int i = 0; i < 4; ++i) {
+        const int col = kColsPerWave * w + (4 * g + i) * 8;
+        if (pc.complete) {
+          u32x4_t pk;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(acc[q][2 * u][i] * scale, acc[q][2 * u + 1][i] * scale);
+          *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
+        } else {
+          f32x4_t v0, v1;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v0[u] = acc[q][u][i] * scale;
+            v1[u] = acc[q][4 + u][i] * scale;
+          }
+          f32x4_t* dst =
+              reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + c16) * kVDim + col);
+          dst[0] = v0;
+          dst[1] = v1;
+        }
+      }
+    } else if (pc.complete) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         u32x4_t pk;
 #pragma unroll
         for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(acc[q][2 * u][i] * scale, acc[q][2 * u + 1][i] * scale);
-        *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
-      } else {
+        *reinterpret_cast<u32x4_t*>(stage + c16 * kOutPitchBf16 + (4 * g + i) * 16) = pk;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < kHeads / 4; ++r) {
+        const int h = 4 * r + (lane >> 4);
+        const int c = lane & 15;  // 16-byte piece of the head's 256 bytes
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + h * kOutPitchBf16 + c * 16);
+        *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + h) * kVDim + kColsPerWave * w + c * 8) = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         f32x4_t v0, v1;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           v0[u] = acc[q][u][i] * scale;
           v1[u] = acc[q][4 + u][i] * scale;
         }
-        f32x4_t* dst =
-            reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + c16) * kVDim + col);
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(stage + c16 * kOutPitchF32 + (4 * g + i) * 32);
         dst[0] = v0;
         dst[1] = v1;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < kHeads / 2; ++r) {
+        const int h = 2 * r + (lane >> 5);
+        const int c = lane & 31;  // 16-byte piece of the head's 512 bytes
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + h * kOutPitchF32 + c * 16);
+        *reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + h) * kVDim + kColsPerWave * w +
+                                    c * 4) = v;
       }
     }
     if (!pc.complete && w == 0 && g == 0)
