@@ -830,6 +830,13 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       nsrc = tile_src(idxn[k], tt + D);
       idxn[k] = page_index(tt + 2 * D);
     }
+    // bf16 Q over fp8 K: chunk j + 1 is widened while chunk j's products run
+    // (the fences around each refill would otherwise keep them apart)
+    bf16x8_t wk0, wk1;
+    if constexpr (QT == Dt::BF16 && KT == Dt::FP8) {
+      wk0 = fp8x8_to_bf16x8(dat[k][0][0], dat[k][0][1]);
+      wk1 = fp8x8_to_bf16x8(dat[k][0][2], dat[k][0][3]);
+    }
 #pragma unroll
     for (int j = 0; j < L::kChunks; ++j) {
       const u32x4_t kk = dat[k][j];
@@ -844,8 +851,12 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
             s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[q][j], s0[q], 0, 0, 0);
         }
       } else if constexpr (QT == Dt::BF16) {
-        const bf16x8_t k0 = fp8x8_to_bf16x8(kk[0], kk[1]);
-        const bf16x8_t k1 = fp8x8_to_bf16x8(kk[2], kk[3]);
+        const bf16x8_t k0 = wk0;
+        const bf16x8_t k1 = wk1;
+        if (j + 1 < L::kChunks) {
+          wk0 = fp8x8_to_bf16x8(dat[k][j + 1][0], dat[k][j + 1][1]);
+          wk1 = fp8x8_to_bf16x8(dat[k][j + 1][2], dat[k][j + 1][3]);
+        }
 #pragma unroll
         for (int q = 0; q < QL; ++q) {
           s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[q][2 * j], s0[q], 0, 0, 0);
