@@ -254,7 +254,7 @@ def main() -> int:
     sm_scale = 1.0 / 24.0
     stream = torch.cuda.current_stream()
 
-    def step(i: int, ev=None):
+    def step(i: int, ev=None, ev_merge=None):
         r = i % R
         if dynamic_q:
             binding.mla_decode_quantize_q_dynamic(q_bf16, q_in, q_scale, scratch, stream)
@@ -266,7 +266,11 @@ def main() -> int:
                                   sm_scale, out, stream)
         if ev is not None:
             ev[1].record(stream)
+        if ev_merge is not None:
+            ev_merge[0].record(stream)
         binding.mla_decode_merge(dec.plan, qo_indptr, kv_indptr, out, stream)
+        if ev_merge is not None:
+            ev_merge[1].record(stream)
 
     # every event is created before the warm-up, so no host work idles the GPU between the two timed regions
     t_start = torch.cuda.Event(enable_timing=True)
@@ -305,6 +309,12 @@ def main() -> int:
     torch.cuda.synchronize()
     hot_ms = sorted(a.elapsed_time(b) for a, b in evs[:n_diag])
     hot_med_ms = hot_ms[len(hot_ms) // 2]
+    # the merge launch alone (rotating KV copies as in the timed regions)
+    for i in range(n_diag):
+        step(i, None, evs[i])
+    torch.cuda.synchronize()
+    merge_ms = sorted(a.elapsed_time(b) for a, b in evs[:n_diag])
+    merge_avg_ms = sum(merge_ms) / len(merge_ms)
     torch.cuda.synchronize()
     plan_t0 = time.perf_counter()
     for _ in range(20):
@@ -340,10 +350,29 @@ def main() -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     probe_gbs = probe.numel() * 10 / (t_start.elapsed_time(t_end) * 1e-3) / 1e9
-    del probe, sink
-
+    del probe
+    # the same probe over exactly the attention launch's algorithmic bytes (rounded up to 16), one launch per
+    # slice, rotating over slices that together exceed the last-level cache: the plain read rate at this size,
+    # start-up and tail included, as the attention launch pays them
     q_elt = 1 if sep_cast else 2  # the attention launch reads fp8 Q, or bf16 Q it casts itself
     alg_bytes = algorithmic_bytes(spec, case, q_elt)
+    n_slice = (alg_bytes + 15) // 16 * 16
+    n_rot = max(2, math.ceil(args.rotate_bytes / n_slice))
+    slab = torch.ones(n_slice * n_rot, dtype=torch.uint8, device=dev)
+    slices = [slab[i * n_slice:(i + 1) * n_slice] for i in range(n_rot)]
+    for i in range(2 * n_rot):
+        binding.mla_read_probe(slices[i % n_rot], sink, stream)
+    torch.cuda.synchronize()
+    same_ms = []
+    for i in range(n_diag):
+        evs[i][0].record(stream)
+        binding.mla_read_probe(slices[i % n_rot], sink, stream)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    same_ms = sorted(a.elapsed_time(b) for a, b in evs[:n_diag])
+    same_avg_ms = sum(same_ms) / len(same_ms)
+    del slab, slices, sink
+
     q_prep = 0
     if dynamic_q:
         q_prep = q_bf16.numel() * 5  # amax pass reads 2 B, cast pass reads 2 B and writes 1 B per value
@@ -414,12 +443,22 @@ def main() -> int:
         },
         "diagnostics": {
             "attention_median_us_one_kv_copy_reused": round(hot_med_ms * 1e3, 2),
+            "merge_avg_us": round(merge_avg_ms * 1e3, 2),
             "plan_us_per_call_host": round(plan_us, 1),
             "q_cast_us": cast_us,
             "read_probe": {
                 "kind": "mla_read_probe: 16-byte streaming reads of 1 GiB, 1024 workgroups x 256 threads, same device",
                 "GBps": round(probe_gbs, 1),
                 "attention_frac_of_probe": round(achieved / probe_gbs, 4),
+            },
+            "read_probe_same_bytes": {
+                "kind": "mla_read_probe over the attention launch's algorithmic bytes, one launch each, "
+                        f"rotating over {n_rot} slices",
+                "bytes": n_slice,
+                "avg_us": round(same_avg_ms * 1e3, 2),
+                "GBps": round(n_slice / (same_avg_ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(n_slice / (same_avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "attention_time_over_probe": round(kern_avg_ms / same_avg_ms, 4),
             },
         },
         "wall_s_timed": round(wall, 4),

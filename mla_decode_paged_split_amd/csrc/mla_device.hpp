@@ -270,10 +270,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Stores of results (bf16 rows, float32 partials and their lse) carry the
-// non-temporal hint: nothing in the launch reads them back, and lines that do
-// not linger dirty in the L2 shorten the write-back at the end of the launch
-// (the attention launch ran 0.8-1.1 us shorter on 64 x 8192 and 64 x 1024
-// batches than with plain stores).
+// non-temporal hint: nothing in the same launch reads them back, and lines
+// that do not linger dirty in the L2 shorten the write-back at the end of the
+// launch (the attention launch ran 0.8-1.1 us shorter on 64 x 8192 and
+// 64 x 1024 batches than with plain stores).
 __device__ __forceinline__ void st_stream(const u32x4_t& v, uint16_t* dst) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
 }
@@ -498,7 +498,7 @@ __device__ void merge_head_wave(const float* __restrict__ part_o, const float* _
   pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
   pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
   pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
-  *reinterpret_cast<u32x4_t*>(out_head + lane * 8) = pk;
+  st_stream(pk, out_head + lane * 8);
 }
 
 // ------------------------------------------------------------- zero output
@@ -1297,6 +1297,9 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int b = blockIdx.x;
   const int h = blockIdx.y;
   const int tau = blockIdx.z;
+  // Every index this wave needs is loaded first, in one round trip: a load
+  // written after one of the early exits below is issued only once the values
+  // that decide the exit have arrived.
   const int32_t* gr = a.counters + a.batch;  // the split the attention launch used
   Geo geo;
   geo.base = gr[0];
@@ -1304,18 +1307,18 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   geo.total = gr[2];
   geo.chunk = gr[3];
   geo.n_wg = gr[4];
-  const int st = a.kv_indptr[b] - geo.base + geo.cost * b;
-  const int en = st + (a.kv_indptr[b + 1] - a.kv_indptr[b]);
-  if (en <= st) return;
+  const int ipb = a.kv_indptr[b];
+  const int ipe = a.kv_indptr[b + 1];
+  const int qo = a.qo_indptr[b];
+  const int qo_e = a.qo_indptr[b + 1];
+  const int st = ipb - geo.base + geo.cost * b;
+  const int en = st + (ipe - ipb);
+  const int q_len = a.max_q_len > 1 ? min(max(qo_e - qo, 0), a.max_q_len) : 1;
   // A split that does not hold this sequence (none recorded yet: chunk 0, or
   // another kv_indptr) is skipped: every slot read below is then < 2 * n_wg
   // <= 2 * units, inside the partial buffers.
+  if (en <= st || tau >= q_len) return;
   if (geo.chunk < 1 || geo.n_wg > a.units || st < 0 || en > geo.total || (en - 1) / geo.chunk >= geo.n_wg) return;
-  const int qo = a.qo_indptr[b];
-  if (a.max_q_len > 1) {
-    const int q_len = min(max(a.qo_indptr[b + 1] - qo, 0), a.max_q_len);
-    if (tau >= q_len) return;
-  }
   const int S = piece_count(st, en, geo.chunk);
   if (S <= 1) return;
   const int chunk = geo.chunk;
