@@ -12,7 +12,7 @@ Two kinds of summary:
 
 Usage:
   python -m mla_decode_paged_split_amd.profile_summary trace <stats.csv> <out.md> "<command>" \
-      [<trace.csv> <timed steps> <bench log>]
+      [<trace.csv> <warm-up steps> <timed steps> <bench log>]
   python -m mla_decode_paged_split_amd.profile_summary pmc <workload> <fetch.csv> <write.csv> \
       <copy_fetch.csv> <copy_write.csv> <algorithmic_bytes> <out.json> "<commands>"
   python -m mla_decode_paged_split_amd.profile_summary mfma <counters.csv> <out.md> "<command>" <flops> <peak>
@@ -41,10 +41,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | None = None, steps: int = 0,
-                  bench_log: str | None = None) -> None:
-    """The --stats table, plus (with the per-dispatch trace) the attention launches of the bench's last
-    timed region, which are the launches its HIP events time, and the bench's own line from that run."""
+def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | None = None, warmup: int = 0,
+                  steps: int = 0, bench_log: str | None = None) -> None:
+    """The --stats table, plus (with the per-dispatch trace) the attention launches of the bench's second
+    timed region, which are the launches its HIP events time (the bench issues warm-up, then the steps of
+    region 1, then those of region 2, then its diagnostics), and the bench's own line from that run."""
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [
         "# Kernel trace summary",
@@ -66,11 +67,11 @@ def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | No
     if trace_csv and steps > 0:
         d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(open(trace_csv))
              if ATTENTION in r["Kernel_Name"]]
-        last = d[-steps:]
+        last = d[warmup + steps:warmup + 2 * steps]
         lines += [
             "",
-            f"Attention launches of the event-timed region (the last {len(last)} of {len(d)}): "
-            f"mean {statistics.mean(last):.2f} us, median {statistics.median(last):.2f} us, "
+            f"Attention launches of the event-timed region (launches {warmup + steps + 1}-{warmup + 2 * steps} "
+            f"of {len(d)}): mean {statistics.mean(last):.2f} us, median {statistics.median(last):.2f} us, "
             f"min {min(last):.2f} us, max {max(last):.2f} us.",
         ]
     if bench_log:
@@ -172,7 +173,8 @@ if __name__ == "__main__":
     kind = sys.argv[1]
     if kind == "trace":
         trace_summary(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:6] or [None]),
-                      int(sys.argv[6]) if len(sys.argv) > 6 else 0, *(sys.argv[7:8] or [None]))
+                      int(sys.argv[6]) if len(sys.argv) > 6 else 0, int(sys.argv[7]) if len(sys.argv) > 7 else 0,
+                      *(sys.argv[8:9] or [None]))
     elif kind == "mfma":
         mfma_summary(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), float(sys.argv[6]))
     elif kind == "pmc":
