@@ -269,11 +269,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Stores of results (bf16 rows, float32 partials and their lse) carry the
+// Stores of whole runs of results (bf16 rows, float32 partials and their
+// lse, staged so that each store instruction covers whole lines) carry the
 // non-temporal hint: nothing in the same launch reads them back, and lines
 // that do not linger dirty in the L2 shorten the write-back at the end of the
 // launch (the attention launch ran 0.8-1.1 us shorter on 64 x 8192 and
-// 64 x 1024 batches than with plain stores).
+// 64 x 1024 batches than with plain stores).  Stores that write 16 bytes into
+// each of 64 lines keep the plain form: with the hint the partial lines are
+// not merged in the L2 (two causal tokens per pass ran ~21 us longer on a
+// 64 x 8192 batch).
 __device__ __forceinline__ void st_stream(const u32x4_t& v, uint16_t* dst) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
 }
@@ -1005,7 +1009,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
           u32x4_t pk;
 #pragma unroll
           for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(acc[q][2 * u][i] * scale, acc[q][2 * u + 1][i] * scale);
-          st_stream(pk, a.out + ((size_t)t * kHeads + c16) * kVDim + col);
+          *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
         } else {
           f32x4_t v0, v1;
 #pragma unroll
@@ -1013,9 +1017,10 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
             v0[u] = acc[q][u][i] * scale;
             v1[u] = acc[q][4 + u][i] * scale;
           }
-          float* dst = a.part_o + ((size_t)(pc.slot + q) * kHeads + c16) * kVDim + col;
-          st_stream(v0, dst);
-          st_stream(v1, dst + 4);
+          f32x4_t* dst =
+              reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + c16) * kVDim + col);
+          dst[0] = v0;
+          dst[1] = v1;
         }
       }
     } else if (pc.complete) {
