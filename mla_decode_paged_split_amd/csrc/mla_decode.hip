@@ -93,28 +93,35 @@ int ilog2(int v) {
 
 // QL query tokens per walk of a piece; batches beyond the kernel's LDS
 // sequence table read the indptrs from memory.
-template <mla::Dt QT, mla::Dt KT, int QL, bool kGeneral>
+template <mla::Dt QT, mla::Dt KT, int QL, int kForm>
 hipError_t launch_attention_ql(const mla::Args& a, hipStream_t stream) {
   if (a.batch <= mla::kSeqTable)
-    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, false, QL, kGeneral>), dim3(a.units), dim3(mla::kThreads), 0,
+    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, false, QL, kForm>), dim3(a.units), dim3(mla::kThreads), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, true, QL, kGeneral>), dim3(a.units), dim3(mla::kThreads), 0,
+    hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, true, QL, kForm>), dim3(a.units), dim3(mla::kThreads), 0,
                        stream, a);
   return hipGetLastError();
+}
+
+template <mla::Dt QT, mla::Dt KT, int QL>
+hipError_t launch_attention_general(const mla::Args& a, hipStream_t stream) {
+  return a.logit_cap > 0.f ? launch_attention_ql<QT, KT, QL, 2>(a, stream)
+                           : launch_attention_ql<QT, KT, QL, 1>(a, stream);
 }
 
 // The plain decode (pages of one row, one token per sequence, no soft-cap)
 // runs a kernel with the page arithmetic and the cap compiled out.  Otherwise
 // fp8 KV serves two tokens per walk of a piece and bf16 KV (twice the row
-// bytes in the register ring) walks a piece once per token.
+// bytes in the register ring) walks a piece once per token, in a form with
+// the cap compiled in or out.
 template <mla::Dt QT, mla::Dt KT>
 hipError_t launch_attention(const mla::Args& a, hipStream_t stream) {
   const bool general = a.page_shift > 0 || a.max_q_len > 1 || a.logit_cap > 0.f;
-  if (!general) return launch_attention_ql<QT, KT, 1, false>(a, stream);
+  if (!general) return launch_attention_ql<QT, KT, 1, 0>(a, stream);
   if constexpr (KT == mla::Dt::FP8)
-    if (a.max_q_len > 1) return launch_attention_ql<QT, KT, 2, true>(a, stream);
-  return launch_attention_ql<QT, KT, 1, true>(a, stream);
+    if (a.max_q_len > 1) return launch_attention_general<QT, KT, 2>(a, stream);
+  return launch_attention_general<QT, KT, 1>(a, stream);
 }
 
 // The plan-derived launch arguments shared by the attention and merge

@@ -604,10 +604,12 @@ struct Logit {
   float c_score;
   float k1;
   float k2;
-  int capped;  // workgroup-uniform: decided once per tile, not per score
-  template <bool kGeneral>
+  // The cap is a kernel form of its own, not a runtime branch: given a
+  // runtime choice the compiler evaluated both forms for every score (eight
+  // more exp2 and reciprocals per step with two tokens) and selected.
+  template <bool kCap>
   __device__ __forceinline__ void apply(const f32x4_t& sc, float (&y)[4]) const {
-    if (kGeneral && capped) {
+    if constexpr (kCap) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = fast_exp2(sc[i] * k1);
@@ -624,7 +626,7 @@ struct Logit {
 // threads take part; the workgroup writes either the final bf16 rows
 // (complete) or the float32 partials.  kGeneral = false is the plain decode
 // (pages of one row, no soft-cap), with both compiled out of the loop.
-template <Dt QT, Dt KT, int QL, bool kGeneral, class RingT>
+template <Dt QT, Dt KT, int QL, bool kGeneral, bool kCap, class RingT>
 __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& pc, const Logit logit,
                              float out_mul, RingT& ring) {
   using L = KvLayout<KT>;
@@ -902,7 +904,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     for (int q = 0; q < QL; ++q) {
       const f32x4_t sc = s0[q] + s1[q];
       float y[4];
-      logit.apply<kGeneral>(sc, y);
+      logit.apply<kCap>(sc, y);
       mx[q] = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1078,8 +1080,13 @@ __device__ __forceinline__ int pack_seq_aux(const Args& a, int qo_b, int qo_e, i
   return (ql << 16) | last;
 }
 
-template <Dt QT, Dt KT, bool kBigBatch, int QL, bool kGeneral>
+// kForm 0: the plain decode (pages of one row, one token, no cap); 1: the
+// general form without the soft-cap; 2: the general form with it.
+template <Dt QT, Dt KT, bool kBigBatch, int QL, int kForm>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
+  static_assert(kForm >= 0 && kForm <= 2, "three kernel forms");
+  constexpr bool kGeneral = kForm > 0;
+  constexpr bool kCap = kForm == 2;
   static_assert(kGeneral || QL == 1, "several tokens per walk only in the general form");
   __shared__ Smem<KT, QL> sm;
   const int sh = kGeneral ? a.page_shift : 0;
@@ -1175,8 +1182,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   const float c_nat = a.sm_scale * qs * ks;
   Logit logit;
   logit.c_score = c_nat * kLog2e;
-  logit.capped = a.logit_cap > 0.f ? 1 : 0;
-  logit.k1 = logit.capped ? 2.0f * kLog2e * c_nat / a.logit_cap : 0.f;
+  logit.k1 = kCap ? 2.0f * kLog2e * c_nat / a.logit_cap : 0.f;
   logit.k2 = a.logit_cap * kLog2e;
   const float out_mul = ks;
 
@@ -1248,7 +1254,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       pc.slot = complete ? -1 : slot * a.max_q_len + tau0;
       pc.complete = complete;
       if (!primed || b != bmin || tau0 != 0) issue_ring_indices(a.kv_indices, pc.ip0, nrows, sh, ring);
-      attend_piece<QT, KT, QL, kGeneral>(a, sm, pc, logit, out_mul, ring);
+      attend_piece<QT, KT, QL, kGeneral, kCap>(a, sm, pc, logit, out_mul, ring);
     }
     if (!complete && a.fused && q_len > 0) {
       __threadfence();
