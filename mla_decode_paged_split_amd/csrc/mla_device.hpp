@@ -534,11 +534,15 @@ __device__ __forceinline__ int page_row(int page, int nrows, int pr, int sh) {
 // The register ring of one piece: the rows of D tiles in flight (tile t in
 // slot t % D) and the row indices of the next D tiles.  Lane (c16, g) of wave
 // w owns row 16w + c16 of every 64-row tile and 16-byte chunks 4j + g of it.
-// Tiles in flight per wave: the layout's depth, one less when two tokens of
-// bf16 Q (72 more registers per token) share the walk.
+// Tiles in flight per wave: the layout's depth, one less when two tokens
+// share the walk.  Two tokens double the products and the softmax, so that
+// walk is bound by its arithmetic rather than by memory, and the registers a
+// deeper ring holds serve the compiler's schedule better (fp8 Q: 1.3 us
+// shorter on a 64 x 8192 batch with a ring of two tiles than of three; bf16 Q
+// needs the room for its second token's 72 registers of Q).
 template <Dt QT, Dt KT, int QL>
 constexpr int ring_depth() {
-  return (QL > 1 && QT == Dt::BF16) ? KvLayout<KT>::kDepth - 1 : KvLayout<KT>::kDepth;
+  return QL > 1 ? KvLayout<KT>::kDepth - 1 : KvLayout<KT>::kDepth;
 }
 
 template <Dt KT, int Depth>
