@@ -363,7 +363,6 @@ def main() -> int:
     for i in range(2 * n_rot):
         binding.mla_read_probe(slices[i % n_rot], sink, stream)
     torch.cuda.synchronize()
-    same_ms = []
     for i in range(n_diag):
         evs[i][0].record(stream)
         binding.mla_read_probe(slices[i % n_rot], sink, stream)
