@@ -176,6 +176,33 @@ def test_constant_v_returns_constant(gpu):
     assert err <= float(c.float().abs().max()) * 2.0 ** -8
 
 
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_zero_q_returns_mean_of_v(gpu, qd, kd):
+    """q = 0 makes every score 0, so each output is the plain mean of its sequence's V rows.
+
+    Every weight is exactly 1 (2^0), split or not, so the only rounding is the float32 sum, the
+    merge's float32 weights and the bf16 output: the result must lie within 2^-8 max|v| of the
+    float64 mean, for every split tried and with the fp8 cast of Q in the kernel too.
+    """
+    spec = synth.CaseSpec(batch=4, q_dtype=qd, kv_dtype=kd, lengths=[1, 37, 700, 2053], permuted=True,
+                          extra_pool_rows=11, seed=1100 + PAIRS.index((qd, kd)))
+    case = synth.make_case(spec)
+    case.q_bf16.zero_()
+    dc = DevCase(case, gpu)
+    scale = float(case.kv_scale[0]) if case.kv_scale is not None else None
+    vals = torch.from_numpy(oracle.decode_operand(case.kv_bits().numpy(), kd, scale))
+    for units, chunk, flags in [(1, 32, 0), (16, 64, 0), (256, 32, 0), (256, 32, 1)]:
+        out = to64(dc.run(num_units=units, min_chunk=chunk, flags=flags, q_cast=qd == "fp8"))
+        for b in range(spec.batch):
+            rows = case.kv_indices[case.kv_indptr[b]:case.kv_indptr[b + 1]].long()
+            v = vals[rows, :512]
+            mean = v.mean(dim=0).numpy()
+            err = np.abs(out[b] - mean[None, :]).max()
+            bound = 2.0 ** -8 * float(v.abs().max())
+            assert err <= bound, (qd, kd, units, chunk, flags, b, err, bound)
+        log(f"  zero q {qd}/{kd} units={units} chunk={chunk} flags={flags}: ok")
+
+
 def test_external_reduce_matches_merge(gpu):
     rng = np.random.default_rng(900)
     counts = [0, 1, 2, 5, 64, 70, 3]
