@@ -203,6 +203,45 @@ def test_zero_q_returns_mean_of_v(gpu, qd, kd):
         log(f"  zero q {qd}/{kd} units={units} chunk={chunk} flags={flags}: ok")
 
 
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_dominant_last_row(gpu, qd, kd):
+    """A row that outscores every other by ~90 (natural log) at the end of each sequence.
+
+    Every head of a sequence's query is the same +-1 vector u, and the sequence's last row (in its
+    logical order) holds c u with c = 4 (bf16 KV; for fp8 KV c = min(4, 400 kv_scale), inside the
+    e4m3 range), so that row scores 24 c >= 48 against a few units for the random rows.  The walk meets it in its last tile, after the running max has settled, so the
+    rescale of everything accumulated so far is taken, and a split sequence's last piece outweighs
+    the others in the merge by ~2^130.  The result must match the oracle and equal that row's V up
+    to the bf16 rounding, with nothing overflowing.
+    """
+    spec = synth.CaseSpec(batch=3, q_dtype=qd, kv_dtype=kd, lengths=[3000, 777, 1500], permuted=True,
+                          extra_pool_rows=5, seed=1200 + PAIRS.index((qd, kd)))
+    case = synth.make_case(spec)
+    gen = torch.Generator().manual_seed(1210)
+    scale = float(case.kv_scale[0]) if case.kv_scale is not None else None
+    for b in range(spec.batch):
+        u = (torch.randint(0, 2, (576,), generator=gen) * 2 - 1).float()
+        case.q_bf16[b] = u.to(torch.bfloat16)  # all 16 heads
+        last = int(case.kv_indices[int(case.kv_indptr[b + 1]) - 1])
+        if kd == "bf16":
+            case.kv[last] = (4 * u).to(torch.bfloat16)
+        else:
+            case.kv[last] = (min(4.0, 400 * scale) * u / scale).to(torch.float8_e4m3fn)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    vals = oracle.decode_operand(case.kv_bits().numpy(), kd, scale)
+    for units, chunk in [(1, 32), (16, 64), (256, 32)]:
+        out = dc.run(num_units=units, min_chunk=chunk, q_cast=qd == "fp8")
+        torch.cuda.synchronize()
+        got = to64(out)
+        assert np.isfinite(got).all()
+        assert_parity(ref, got, f"dominant row {qd}/{kd} units={units}")
+        for b in range(spec.batch):
+            v = vals[int(case.kv_indices[int(case.kv_indptr[b + 1]) - 1]), :512]
+            assert np.abs(got[b] - v[None, :]).max() <= 2.0 ** -8 * np.abs(v).max(), (qd, kd, units, b)
+        log(f"  dominant last row {qd}/{kd} units={units}: ok")
+
+
 def test_external_reduce_matches_merge(gpu):
     rng = np.random.default_rng(900)
     counts = [0, 1, 2, 5, 64, 70, 3]
