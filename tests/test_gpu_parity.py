@@ -242,6 +242,27 @@ def test_dominant_last_row(gpu, qd, kd):
         log(f"  dominant last row {qd}/{kd} units={units}: ok")
 
 
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_shared_and_repeated_pages(gpu, qd, kd):
+    """Sequences that share pages (a common prefix, as with prefix caching) and a sequence that lists
+    pages twice: kv_indices is only followed, so the result must match the oracle on the same indices
+    under every split (a repeated row counts twice in its softmax)."""
+    spec = synth.CaseSpec(batch=3, q_dtype=qd, kv_dtype=kd, lengths=[600, 900, 300], permuted=True,
+                          extra_pool_rows=64, seed=1300 + PAIRS.index((qd, kd)))
+    case = synth.make_case(spec)
+    idx = case.kv_indices.clone()
+    p = case.kv_indptr.tolist()
+    idx[p[1]:p[1] + 400] = idx[p[0]:p[0] + 400]  # sequence 1 starts with sequence 0's first 400 rows
+    idx[p[2] + 150:p[3]] = idx[p[2]:p[2] + 150]  # sequence 2 lists its first 150 rows twice
+    case.kv_indices = idx
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units, chunk in [(1, 32), (16, 64), (256, 32)]:
+        out = dc.run(num_units=units, min_chunk=chunk, q_cast=qd == "fp8")
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"shared pages {qd}/{kd} units={units}")
+
+
 def test_external_reduce_matches_merge(gpu):
     rng = np.random.default_rng(900)
     counts = [0, 1, 2, 5, 64, 70, 3]
