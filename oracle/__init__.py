@@ -27,8 +27,11 @@ cap the plain result) and a 3:1 closed form through atanh(1/2); pages
 against a hand-worked row expansion and against the same rows laid out one
 per page; several query tokens against torch's scaled-dot-product attention
 (no mask, and the square causal mask when every row is a query); the
-amax-scaled cast against torch's float32 division and e4m3fn cast.  No
-function here is "parity unpinned".
+amax-scaled cast against torch's float32 division and e4m3fn cast.  The
+final log-sum-exp: q = 0 gives log n, one row gives its own score, a
+duplicated row adds log 2, scipy's logsumexp over the brute-force scores,
+and the whole equals the merge of its parts' log-sum-exps.  No function here
+is "parity unpinned".
 """
 
 from .formats import (  # noqa: F401
@@ -48,10 +51,13 @@ from .mla import (  # noqa: F401
     V_DIM,
     attention_partial,
     decode_operand,
+    merge_lse,
     merge_partials,
     mla_decode,
     mla_decode_bruteforce,
+    mla_decode_lse,
     mla_decode_sequence,
+    mla_decode_sequence_lse,
     paged_rows,
     soft_cap,
     visible_rows,

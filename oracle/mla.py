@@ -61,9 +61,12 @@ __all__ = [
     "visible_rows",
     "mla_decode",
     "mla_decode_sequence",
+    "mla_decode_sequence_lse",
+    "mla_decode_lse",
     "mla_decode_bruteforce",
     "attention_partial",
     "merge_partials",
+    "merge_lse",
 ]
 
 # kernelindex amd-mixed-mla submission 689529, module constants.
@@ -138,6 +141,65 @@ def mla_decode_sequence(Q: np.ndarray, K: np.ndarray, sm_scale: float, v_dim: in
     P = np.exp(S)
     P /= P.sum(axis=1, keepdims=True)
     return P @ K[:, :v_dim]
+
+
+def mla_decode_sequence_lse(Q: np.ndarray, K: np.ndarray, sm_scale: float, logit_cap: float = 0.0) -> np.ndarray:
+    """Log-sum-exp (natural log) of one sequence's scores: Q [H, D], K [n, D] -> [H].
+
+    ``log sum_j exp(s_j)`` over the n rows, with s the (optionally
+    soft-capped) scores ``sm_scale * Q K^T``: the normaliser of the softmax
+    in ``mla_decode_sequence``.  It is the final-LSE output of the pages'
+    reduce step (submission 690201, ``custom_kernel``: the last argument of
+    ``mla_reduce_v1``, left as None there).  n == 0 gives -inf.
+    """
+    H = Q.shape[0]
+    if K.shape[0] == 0:
+        return np.full(H, -np.inf)
+    S = soft_cap(sm_scale * (Q @ K.T), logit_cap)  # [H, n]
+    mx = S.max(axis=1)
+    return mx + np.log(np.exp(S - mx[:, None]).sum(axis=1))
+
+
+def mla_decode_lse(
+    q_bits: np.ndarray,
+    kv_bits: np.ndarray,
+    qo_indptr: Sequence[int],
+    kv_indptr: Sequence[int],
+    kv_indices: Sequence[int],
+    *,
+    q_dtype: str,
+    kv_dtype: str,
+    q_scale: float | None = None,
+    kv_scale: float | None = None,
+    sm_scale: float = SM_SCALE,
+    sequences: Sequence[int] | None = None,
+    page_size: int = 1,
+    kv_last_page_len: Sequence[int] | None = None,
+    causal: bool = False,
+    logit_cap: float = 0.0,
+) -> np.ndarray:
+    """Log-sum-exp of every query token's scores over the rows it sees: [total_q, H] float64.
+
+    Same inputs and row / token rules as ``mla_decode``; tokens that see no
+    row (and the rows of sequences not in ``sequences``) get -inf.
+    """
+    q_bits = np.asarray(q_bits)
+    kv_bits = np.asarray(kv_bits)
+    qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    kv_indices = np.asarray(kv_indices, dtype=np.int64)
+    total_q, H, _ = q_bits.shape
+    out = np.full((total_q, H), -np.inf)
+    seqs = range(len(kv_indptr) - 1) if sequences is None else sequences
+    for b in seqs:
+        rows = paged_rows(kv_indptr, kv_indices, b, page_size, kv_last_page_len)
+        K = decode_operand(kv_bits[rows], kv_dtype, kv_scale)
+        q_len = int(qo_indptr[b + 1] - qo_indptr[b])
+        for i in range(q_len):
+            t = int(qo_indptr[b]) + i
+            n = visible_rows(len(rows), q_len, i, causal)
+            out[t] = mla_decode_sequence_lse(decode_operand(q_bits[t], q_dtype, q_scale), K[:n], sm_scale, logit_cap)
+    return out
 
 
 def mla_decode(
@@ -253,3 +315,20 @@ def merge_partials(O_parts: np.ndarray, lse_parts: np.ndarray) -> np.ndarray:
     num = np.einsum("sh,shc->hc", w, O_parts)
     out[finite] = num[finite] / z[finite, None]
     return out
+
+
+def merge_lse(lse_parts: np.ndarray) -> np.ndarray:
+    """Log-sum-exp of the whole from the parts' log-sum-exps: [S, H] -> [H].
+
+    ``log sum_i exp(lse_i)``: the rows of all parts together have
+    ``sum_i exp(lse_i)`` as their softmax normaliser.  Parts with lse = -inf
+    add nothing; no parts, or only empty ones, give -inf.
+    """
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    if lse_parts.shape[0] == 0:
+        return np.full(lse_parts.shape[1:], -np.inf)
+    M = lse_parts.max(axis=0)
+    finite = np.isfinite(M)
+    Msafe = np.where(finite, M, 0.0)
+    z = np.where(np.isfinite(lse_parts), np.exp(lse_parts - Msafe[None, :]), 0.0).sum(axis=0)
+    return np.where(finite, Msafe + np.log(np.where(finite, z, 1.0)), -np.inf)

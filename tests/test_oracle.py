@@ -287,6 +287,88 @@ def test_lse_is_log_sum_exp():
     assert np.max(np.abs(lse - np.log(np.exp(s).sum(axis=1)))) <= 1e-12
 
 
+# ------------------------------------------------------------ final log-sum-exp
+
+
+def test_final_lse_zero_query_is_log_n():
+    # every score is 0, so sum_j exp(0) = n
+    rng = np.random.default_rng(31)
+    _, K = _seq(rng, 37)
+    lse = mla.mla_decode_sequence_lse(np.zeros((16, 576)), K, mla.SM_SCALE)
+    assert np.max(np.abs(lse - math.log(37))) <= 1e-14
+
+
+def test_final_lse_single_row_is_its_score():
+    rng = np.random.default_rng(32)
+    Q, K = _seq(rng, 1, 3.0)
+    lse = mla.mla_decode_sequence_lse(Q, K, mla.SM_SCALE)
+    s = [math.fsum(Q[h, d] * K[0, d] for d in range(576)) / 24.0 for h in range(16)]
+    assert np.max(np.abs(lse - np.array(s))) <= 1e-12
+
+
+def test_final_lse_duplicate_row_adds_its_weight():
+    # duplicating every row doubles the sum: + log 2
+    rng = np.random.default_rng(33)
+    Q, K = _seq(rng, 25, 2.0)
+    a = mla.mla_decode_sequence_lse(Q, K, mla.SM_SCALE)
+    b = mla.mla_decode_sequence_lse(Q, np.concatenate([K, K]), mla.SM_SCALE)
+    assert np.max(np.abs(b - a - math.log(2.0))) <= 1e-13
+
+
+def test_final_lse_vs_scipy_logsumexp_of_bruteforce_scores():
+    from scipy.special import logsumexp
+
+    rng = np.random.default_rng(34)
+    lens = [1, 3, 5]
+    q_bits, kv_bits, qo, kvp, idx, _ = _rand_case(rng, 3, lens, permute=True)
+    got = oracle.mla_decode_lse(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16")
+    for b in range(3):
+        Q = formats.decode_bf16(q_bits[b]).tolist()
+        K = [formats.decode_bf16(kv_bits[idx[i]]).tolist() for i in range(kvp[b], kvp[b + 1])]
+        for h in range(16):
+            s = [math.fsum(Q[h][d] * K[j][d] for d in range(576)) / 24.0 for j in range(len(K))]
+            assert abs(logsumexp(s) - got[b, h]) <= 1e-12
+
+
+def test_final_lse_equals_merge_of_part_lses():
+    rng = np.random.default_rng(35)
+    Q, K = _seq(rng, 301, 2.0)
+    bounds = [0, 1, 90, 91, 250, 301]
+    lses = np.stack([mla.attention_partial(Q, K[a:b], mla.SM_SCALE)[1] for a, b in zip(bounds[:-1], bounds[1:])])
+    whole = mla.mla_decode_sequence_lse(Q, K, mla.SM_SCALE)
+    assert np.max(np.abs(mla.merge_lse(lses) - whole)) <= 1e-12
+    # empty parts add nothing; no parts or only empty ones give -inf
+    empty = mla.attention_partial(Q, K[:0], mla.SM_SCALE)[1]
+    assert np.max(np.abs(mla.merge_lse(np.stack([empty, *lses])) - whole)) <= 1e-12
+    assert np.all(np.isneginf(mla.merge_lse(np.stack([empty, empty]))))
+    assert np.all(np.isneginf(mla.merge_lse(np.zeros((0, 16)))))
+
+
+def test_final_lse_soft_cap_limits():
+    # a tiny cap flattens every score to ~0 (log n); a huge cap changes nothing
+    rng = np.random.default_rng(36)
+    Q, K = _seq(rng, 40, 3.0)
+    assert np.max(np.abs(mla.mla_decode_sequence_lse(Q, K, mla.SM_SCALE, logit_cap=1e-9) - math.log(40))) <= 1e-8
+    plain = mla.mla_decode_sequence_lse(Q, K, mla.SM_SCALE)
+    assert np.max(np.abs(mla.mla_decode_sequence_lse(Q, K, mla.SM_SCALE, logit_cap=1e9) - plain)) <= 1e-9
+
+
+def test_final_lse_tokens_and_empty_sequences():
+    # causal token i sees a prefix (its lse is that prefix's); tokens of an empty sequence get -inf
+    rng = np.random.default_rng(37)
+    q_bits = torch.from_numpy(rng.standard_normal((4, 16, 576)).astype(np.float32)).to(torch.bfloat16)
+    q_bits = q_bits.view(torch.int16).numpy()
+    kv = torch.from_numpy(rng.standard_normal((9, 576)).astype(np.float32)).to(torch.bfloat16)
+    kv_bits = kv.view(torch.int16).numpy()
+    qo, kvp, idx = [0, 3, 4], [0, 9, 9], list(range(9))
+    got = oracle.mla_decode_lse(q_bits, kv_bits, qo, kvp, idx, q_dtype="bf16", kv_dtype="bf16", causal=True)
+    K = formats.decode_bf16(kv_bits)
+    for i in range(3):
+        ref = mla.mla_decode_sequence_lse(formats.decode_bf16(q_bits[i]), K[:9 - 2 + i], mla.SM_SCALE)
+        assert np.array_equal(got[i], ref)
+    assert np.all(np.isneginf(got[3]))
+
+
 # -------------------------------------------------------------------- invariants
 
 
