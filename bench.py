@@ -263,12 +263,12 @@ def main() -> int:
         if ev is not None:
             ev[0].record(stream)
         binding.mla_decode_attend(dec.plan, q_in, kvs[r], qo_indptr, kv_indptr, idxs[r], last, q_scale, kv_scale,
-                                  sm_scale, out, stream)
+                                  sm_scale, out, None, stream)
         if ev is not None:
             ev[1].record(stream)
         if ev_merge is not None:
             ev_merge[0].record(stream)
-        binding.mla_decode_merge(dec.plan, qo_indptr, kv_indptr, out, stream)
+        binding.mla_decode_merge(dec.plan, qo_indptr, kv_indptr, out, None, stream)
         if ev_merge is not None:
             ev_merge[1].record(stream)
 

@@ -34,9 +34,18 @@
  *                                   (mla_decode_run_paged only; values are
  *                                   clamped into [1, page_size])
  *   out        [total_q, 16, 512]   bf16
+ *   lse_out    [total_q, 16]        float32, optional (NULL: not written):
+ *                                   the natural-log sum-exp of each token's
+ *                                   scores, log sum_i exp(s_i), over the rows
+ *                                   it sees; -inf where it sees none
  *   q_scale, kv_scale               one float32 each, in device memory
  *                                   (read only for fp8 operands; may be NULL
  *                                   for bf16 operands)
+ *
+ * Alignment: q, kv and out must be 16-byte aligned (the kernels move them in
+ * 16-byte pieces; every row is a multiple of 16 bytes), the index arrays,
+ * scales and lse_out 4-byte aligned.  A misaligned pointer is
+ * MLA_ERR_INVALID_ARG.
  *
  * Supported dtype pairs (q, kv): (bf16, bf16), (bf16, fp8), (fp8, fp8).
  * fp8 is the OCP e4m3fn format (max 448, no infinities).
@@ -71,7 +80,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 2
+#define MLA_DECODE_ABI_VERSION 3
 
 typedef enum {
   MLA_OK = 0,
@@ -146,8 +155,17 @@ typedef struct {
   uint64_t off_part_lse; /* float32 [2 * num_units * max_q_len, 16]: log2-sum-exp of each partial */
 } mla_decode_plan_t;
 
-/* Bytes of device workspace mla_decode_plan needs for these params; 0 if the
- * params are invalid or the device cannot be queried. */
+/*
+ * Bytes of device workspace mla_decode_plan needs for these params; 0 if the
+ * params are invalid or the device cannot be queried.  This is the sizing
+ * half of the pages' per-shape cache (kernelindex amd-mixed-mla submission
+ * 689529, cache builder: get_mla_metadata_info_v1 returns the sizes of the
+ * metadata and work buffers, which are allocated once per shape; submission
+ * 690201 adds the stage-1 intermediates `logits` and `attn_lse` to that
+ * cache).  Here the workspace holds the split partials (float32 O and
+ * log-sum-exp, the counterparts of logits / attn_lse) and a few counters; no
+ * metadata buffer is needed because the split is computed in every launch.
+ */
 size_t mla_decode_workspace_size(const mla_decode_params* params);
 
 /*
@@ -155,6 +173,16 @@ size_t mla_decode_workspace_size(const mla_decode_params* params);
  * the workspace and zero its counters (one small kernel on `stream`).
  * workspace: device memory of at least mla_decode_workspace_size(params)
  * bytes, 256-byte aligned, owned by the caller.  On success *plan is filled.
+ *
+ * This replaces the pages' metadata call (kernelindex amd-mixed-mla
+ * submission 689529, cache builder: get_mla_metadata_v1 turns qo_indptr /
+ * kv_indptr / kv_last_page_len into work lists and reduce maps once per
+ * shape; submission 598454, metadata builder).  Unlike that call it takes no
+ * kv_indptr: the partition of KV rows over workgroups is recomputed on the
+ * device from kv_indptr by every attention launch, so the plan stays valid
+ * while sequence lengths change.  The plan records the device that was
+ * current; later calls with it must run on a stream of that device
+ * (MLA_ERR_INVALID_ARG otherwise).
  */
 mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, size_t workspace_bytes,
                            hipStream_t stream, mla_decode_plan_t* plan);
@@ -187,25 +215,31 @@ mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const vo
  * that launch chose from the workspace.  Before any mla_decode_attend on a
  * plan's workspace it writes nothing; a sequence that does not fit the split
  * found there (another kv_indptr) is skipped, never read out of bounds.
- * Arguments as for mla_decode_run_paged, which is these two calls in order.
+ * Arguments as for mla_decode_run_paged, which is these two calls in order;
+ * both must get the same lse_out (or both NULL): the attention launch writes
+ * it for the sequences it finishes, the merge for the split ones.
  */
 mla_status mla_decode_attend(const mla_decode_plan_t* plan, const void* q, const void* kv,
                              const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                              const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
-                             float sm_scale, void* out, hipStream_t stream);
+                             float sm_scale, void* out, float* lse_out, hipStream_t stream);
 mla_status mla_decode_merge(const mla_decode_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
-                            void* out, hipStream_t stream);
+                            void* out, float* lse_out, hipStream_t stream);
 
 /*
  * mla_decode_run with the rows of each sequence's last page given by
  * kv_last_page_len[b] (device int32 [batch], clamped into [1, page_size];
  * NULL: every page full), as the pages pass kv_last_page_lens next to
- * kv_indptr in pages (submissions 598454 and 641982, pages of 2 and 8 rows).
+ * kv_indptr in pages (submissions 598454 and 641982, pages of 2 and 8 rows),
+ * and optionally the final log-sum-exp of every token and head in lse_out
+ * (float32 [total_q, 16], natural log; NULL: not written).  That is the
+ * output the pages' reduce call leaves unused (submission 690201,
+ * custom_kernel: the last argument of mla_reduce_v1 is None).
  */
 mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, const void* kv,
                                 const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                                 const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
-                                float sm_scale, void* out, hipStream_t stream);
+                                float sm_scale, void* out, float* lse_out, hipStream_t stream);
 
 /*
  * Step a0 for fp8 queries: cast n bf16 values to fp8 e4m3fn with
@@ -241,11 +275,17 @@ mla_status mla_decode_quantize_q_dynamic(const void* q_bf16, void* q_fp8, float*
  *   part_o   [n_parts, 16, 512] float32, softmax-normalised over each part
  *   part_lse [n_parts, 16] float32, natural-log sum-exp of each part's scores
  *   out      [batch, 16, 512] bf16
- * Parts with lse = -inf carry no weight; a sequence whose parts are all empty
- * (or that has none) gets zeros.
+ *   lse_out  [batch, 16] float32 or NULL: log sum_p exp(lse[p,h]), the
+ *            natural-log sum-exp over all parts (the reduce's final-LSE
+ *            output, which submission 690201 passes as None)
+ * Parts with lse = -inf carry no weight and their part_o rows are ignored
+ * (they may hold NaN, e.g. 0/0 of an empty shard); a sequence whose parts
+ * are all empty (or that has none) gets zeros and lse -inf.  A NaN lse makes
+ * that head's output and lse NaN.  part_o and out
+ * must be 16-byte aligned, part_lse, part_indptr and lse_out 4-byte aligned.
  */
 mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const int32_t* part_indptr,
-                             int32_t batch, void* out, hipStream_t stream);
+                             int32_t batch, void* out, float* lse_out, hipStream_t stream);
 
 /*
  * Diagnostic, not part of the decode path: read `bytes` of device memory at
@@ -260,7 +300,8 @@ mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const i
 #define MLA_READ_PROBE_SINK_WORDS 1024
 mla_status mla_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream);
 
-/* Static description of a status code. */
+/* Static description of a status code.  Derived: the pages define no error
+ * reporting (their calls raise Python exceptions), so no passage backs it. */
 const char* mla_status_string(mla_status status);
 
 /* MLA_DECODE_ABI_VERSION of the built library. */

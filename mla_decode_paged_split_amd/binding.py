@@ -123,17 +123,17 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
         L.mla_decode_run.restype = ctypes.c_int
         L.mla_decode_run_paged.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
-                                           vp]
+                                           vp, vp]
         L.mla_decode_run_paged.restype = ctypes.c_int
         L.mla_decode_attend.argtypes = L.mla_decode_run_paged.argtypes
         L.mla_decode_attend.restype = ctypes.c_int
-        L.mla_decode_merge.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp]
+        L.mla_decode_merge.argtypes = [ctypes.POINTER(MlaDecodePlan), vp, vp, vp, vp, vp]
         L.mla_decode_merge.restype = ctypes.c_int
         L.mla_decode_quantize_q.argtypes = [vp, vp, i64, vp]
         L.mla_decode_quantize_q.restype = ctypes.c_int
         L.mla_decode_quantize_q_dynamic.argtypes = [vp, vp, vp, vp, sz, i64, vp]
         L.mla_decode_quantize_q_dynamic.restype = ctypes.c_int
-        L.mla_decode_reduce.argtypes = [vp, vp, vp, i32, vp, vp]
+        L.mla_decode_reduce.argtypes = [vp, vp, vp, i32, vp, vp, vp]
         L.mla_decode_reduce.restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -213,12 +213,14 @@ def mla_decode_plan(params: MlaDecodeParams, workspace: torch.Tensor, stream=Non
     return plan
 
 
-def _check_index_args(out, **ints) -> None:
+def _check_index_args(out, lse_out=None, **ints) -> None:
     for name, t in ints.items():
         if t is not None and t.dtype != torch.int32:
             raise ValueError(f"{name} must be int32")
     if out.dtype != torch.bfloat16:
         raise ValueError("out must be bf16")
+    if lse_out is not None and (lse_out.dtype != torch.float32 or lse_out.numel() * 512 < out.numel()):
+        raise ValueError("lse_out must be float32 with one value per token and head")
 
 
 def mla_decode_run(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
@@ -234,31 +236,32 @@ def mla_decode_run(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_in
 def mla_decode_run_paged(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
                          kv_indptr: torch.Tensor, kv_indices: torch.Tensor, kv_last_page_len: Optional[torch.Tensor],
                          q_scale: Optional[torch.Tensor], kv_scale: Optional[torch.Tensor], sm_scale: float,
-                         out: torch.Tensor, stream=None) -> None:
-    _check_index_args(out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                         out: torch.Tensor, lse_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check_index_args(out, lse_out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
                       kv_last_page_len=kv_last_page_len)
     code = lib().mla_decode_run_paged(ctypes.byref(plan), _ptr(q), _ptr(kv), _ptr(qo_indptr), _ptr(kv_indptr),
                                       _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(q_scale), _ptr(kv_scale),
-                                      float(sm_scale), _ptr(out), _stream(stream))
+                                      float(sm_scale), _ptr(out), _ptr(lse_out), _stream(stream))
     _check(code, "mla_decode_run_paged")
 
 
 def mla_decode_attend(plan: MlaDecodePlan, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
                       kv_indptr: torch.Tensor, kv_indices: torch.Tensor, kv_last_page_len: Optional[torch.Tensor],
                       q_scale: Optional[torch.Tensor], kv_scale: Optional[torch.Tensor], sm_scale: float,
-                      out: torch.Tensor, stream=None) -> None:
-    _check_index_args(out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                      out: torch.Tensor, lse_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check_index_args(out, lse_out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
                       kv_last_page_len=kv_last_page_len)
     code = lib().mla_decode_attend(ctypes.byref(plan), _ptr(q), _ptr(kv), _ptr(qo_indptr), _ptr(kv_indptr),
                                    _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(q_scale), _ptr(kv_scale),
-                                   float(sm_scale), _ptr(out), _stream(stream))
+                                   float(sm_scale), _ptr(out), _ptr(lse_out), _stream(stream))
     _check(code, "mla_decode_attend")
 
 
 def mla_decode_merge(plan: MlaDecodePlan, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, out: torch.Tensor,
-                     stream=None) -> None:
-    _check_index_args(out, qo_indptr=qo_indptr, kv_indptr=kv_indptr)
-    code = lib().mla_decode_merge(ctypes.byref(plan), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(out), _stream(stream))
+                     lse_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check_index_args(out, lse_out, qo_indptr=qo_indptr, kv_indptr=kv_indptr)
+    code = lib().mla_decode_merge(ctypes.byref(plan), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(out), _ptr(lse_out),
+                                  _stream(stream))
     _check(code, "mla_decode_merge")
 
 
@@ -282,12 +285,14 @@ def mla_decode_quantize_q_dynamic(q_bf16: torch.Tensor, q_fp8: torch.Tensor, q_s
 
 
 def mla_decode_reduce(part_o: torch.Tensor, part_lse: torch.Tensor, part_indptr: torch.Tensor, out: torch.Tensor,
-                      stream=None) -> None:
+                      lse_out: Optional[torch.Tensor] = None, stream=None) -> None:
     if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32 or part_indptr.dtype != torch.int32:
         raise ValueError("partials must be float32 and part_indptr int32")
+    if lse_out is not None and (lse_out.dtype != torch.float32 or lse_out.numel() * 512 < out.numel()):
+        raise ValueError("lse_out must be float32 with one value per sequence and head")
     batch = part_indptr.numel() - 1
     code = lib().mla_decode_reduce(_ptr(part_o), _ptr(part_lse), _ptr(part_indptr), batch, _ptr(out),
-                                   _stream(stream))
+                                   _ptr(lse_out), _stream(stream))
     _check(code, "mla_decode_reduce")
 
 
@@ -308,11 +313,14 @@ class Decoder:
         self.kv_dtype = kv_dtype
 
     def run(self, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out, stream=None,
-            kv_last_page_len=None):
-        if kv_last_page_len is None:
+            kv_last_page_len=None, lse_out=None):
+        if lse_out is not None:
+            mla_decode_run_paged(self.plan, q, kv, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_scale,
+                                 kv_scale, sm_scale, out, lse_out, stream)
+        elif kv_last_page_len is None:
             mla_decode_run(self.plan, q, kv, qo_indptr, kv_indptr, kv_indices, q_scale, kv_scale, sm_scale, out,
                            stream)
         else:
             mla_decode_run_paged(self.plan, q, kv, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_scale,
-                                 kv_scale, sm_scale, out, stream)
+                                 kv_scale, sm_scale, out, None, stream)
         return out

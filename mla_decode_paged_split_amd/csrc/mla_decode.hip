@@ -85,6 +85,20 @@ Layout layout_for(const mla_decode_params* p, int32_t units) {
   return L;
 }
 
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The device a launch on `stream` runs on (the null stream: the current device).
+mla_status stream_device(hipStream_t stream, int32_t* device) {
+  int dev = 0;
+  if (stream == nullptr) {
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  } else if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    return MLA_ERR_HIP;
+  }
+  *device = dev;
+  return MLA_OK;
+}
+
 int ilog2(int v) {
   int s = 0;
   while ((1 << s) < v) ++s;
@@ -125,9 +139,10 @@ hipError_t launch_attention(const mla::Args& a, hipStream_t stream) {
 }
 
 // The plan-derived launch arguments shared by the attention and merge
-// launches; checks the plan and the pointers both launches read.
+// launches; checks the plan and the pointers both launches read.  The
+// stream's device is checked last: it is the only check that calls HIP.
 mla_status make_args(const mla_decode_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr, void* out,
-                     mla::Args* a) {
+                     float* lse_out, hipStream_t stream, mla::Args* a) {
   if (plan == nullptr) return MLA_ERR_INVALID_ARG;
   const mla_decode_params& p = plan->params;
   mla_status st = validate_params(&p);
@@ -136,12 +151,19 @@ mla_status make_args(const mla_decode_plan_t* plan, const int32_t* qo_indptr, co
   if (plan->workspace == nullptr || plan->workspace_bytes < layout_for(&p, p.num_units).total)
     return MLA_ERR_WORKSPACE;
   if (qo_indptr == nullptr || kv_indptr == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned(qo_indptr, 4) || !aligned(kv_indptr, 4) || !aligned(out, 16) || !aligned(lse_out, 4))
+    return MLA_ERR_INVALID_ARG;
+  int32_t dev = 0;
+  st = stream_device(stream, &dev);
+  if (st != MLA_OK) return st;
+  if (dev != plan->device) return MLA_ERR_INVALID_ARG;
   uint8_t* ws = static_cast<uint8_t*>(plan->workspace);
   memset(a, 0, sizeof(*a));
   a->qo_indptr = qo_indptr;
   a->kv_indptr = kv_indptr;
   a->logit_cap = p.logit_cap;
   a->out = static_cast<uint16_t*>(out);
+  a->lse_out = lse_out;
   a->part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
   a->part_lse = reinterpret_cast<float*>(ws + plan->off_part_lse);
   a->counters = reinterpret_cast<int32_t*>(ws + plan->off_counters);
@@ -238,15 +260,20 @@ mla_status mla_decode_plan(const mla_decode_params* params, void* workspace, siz
 mla_status mla_decode_attend(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,
                              const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
                              const float* q_scale, const float* kv_scale, float sm_scale, void* out,
-                             hipStream_t stream) {
-  mla::Args a;
-  mla_status st = make_args(plan, qo_indptr, kv_indptr, out, &a);
-  if (st != MLA_OK) return st;
+                             float* lse_out, hipStream_t stream) {
+  if (plan == nullptr) return MLA_ERR_INVALID_ARG;
   const mla_decode_params& p = plan->params;
+  // pointer checks first: they need no HIP call
   if (q == nullptr || kv == nullptr || kv_indices == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(kv_indices, 4) || !aligned(kv_last_page_len, 4) ||
+      !aligned(q_scale, 4) || !aligned(kv_scale, 4))
+    return MLA_ERR_INVALID_ARG;
   if (p.q_dtype == MLA_DTYPE_FP8_E4M3FN && q_scale == nullptr) return MLA_ERR_INVALID_ARG;
   if (p.kv_dtype == MLA_DTYPE_FP8_E4M3FN && kv_scale == nullptr) return MLA_ERR_INVALID_ARG;
   if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return MLA_ERR_INVALID_ARG;
+  mla::Args a;
+  mla_status st = make_args(plan, qo_indptr, kv_indptr, out, lse_out, stream, &a);
+  if (st != MLA_OK) return st;
   a.q = q;
   a.kv = kv;
   a.kv_indices = kv_indices;
@@ -266,9 +293,9 @@ mla_status mla_decode_attend(const mla_decode_plan_t* plan, const void* q, const
 }
 
 mla_status mla_decode_merge(const mla_decode_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
-                            void* out, hipStream_t stream) {
+                            void* out, float* lse_out, hipStream_t stream) {
   mla::Args a;
-  mla_status st = make_args(plan, qo_indptr, kv_indptr, out, &a);
+  mla_status st = make_args(plan, qo_indptr, kv_indptr, out, lse_out, stream, &a);
   if (st != MLA_OK) return st;
   if (a.fused) return MLA_OK;  // the attention launch merged already
   hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(a.batch, mla::kHeads, a.max_q_len), dim3(64), 0, stream, a);
@@ -278,18 +305,18 @@ mla_status mla_decode_merge(const mla_decode_plan_t* plan, const int32_t* qo_ind
 mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, const void* kv,
                                 const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                                 const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
-                                float sm_scale, void* out, hipStream_t stream) {
+                                float sm_scale, void* out, float* lse_out, hipStream_t stream) {
   mla_status st = mla_decode_attend(plan, q, kv, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_scale,
-                                    kv_scale, sm_scale, out, stream);
+                                    kv_scale, sm_scale, out, lse_out, stream);
   if (st != MLA_OK) return st;
-  return mla_decode_merge(plan, qo_indptr, kv_indptr, out, stream);
+  return mla_decode_merge(plan, qo_indptr, kv_indptr, out, lse_out, stream);
 }
 
 mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,
                           const int32_t* kv_indptr, const int32_t* kv_indices, const float* q_scale,
                           const float* kv_scale, float sm_scale, void* out, hipStream_t stream) {
   return mla_decode_run_paged(plan, q, kv, qo_indptr, kv_indptr, kv_indices, nullptr, q_scale, kv_scale, sm_scale,
-                              out, stream);
+                              out, nullptr, stream);
 }
 
 mla_status mla_decode_quantize_q(const void* q_bf16, void* q_fp8, int64_t n, hipStream_t stream) {
@@ -333,12 +360,15 @@ mla_status mla_decode_quantize_q_dynamic(const void* q_bf16, void* q_fp8, float*
 }
 
 mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const int32_t* part_indptr, int32_t batch,
-                             void* out, hipStream_t stream) {
+                             void* out, float* lse_out, hipStream_t stream) {
   if (batch < 1 || part_indptr == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
   if (part_o == nullptr || part_lse == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned(part_o, 16) || !aligned(out, 16) || !aligned(part_lse, 4) || !aligned(part_indptr, 4) ||
+      !aligned(lse_out, 4))
+    return MLA_ERR_INVALID_ARG;
   if (batch > (1 << 30)) return MLA_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(mla::mla_reduce_external_kernel, dim3(batch, mla::kHeads), dim3(64), 0, stream, part_o,
-                     part_lse, part_indptr, static_cast<uint16_t*>(out));
+                     part_lse, part_indptr, static_cast<uint16_t*>(out), lse_out);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

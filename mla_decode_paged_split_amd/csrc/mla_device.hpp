@@ -57,6 +57,7 @@ constexpr int kSplitAlign = 32;           // share sizes are multiples of this
 constexpr int kScanPerThread = 4;         // sequences each thread reads in the first round trip
 constexpr int kSeqTable = kScanPerThread * kThreads;  // sequences whose indptr values are kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;     // log2 growth of the running max tolerated before rescaling
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -138,6 +139,7 @@ struct Args {
   float sm_scale;
   float logit_cap;    // 0: off
   uint16_t* out;      // bf16 bits [total_q, 16, 512]
+  float* lse_out;     // [total_q, 16] natural-log sum-exp of each token's scores, or null
   float* part_o;      // [2*units*max_q_len, 16, 512]
   float* part_lse;    // [2*units*max_q_len, 16], log2 domain
   int32_t* counters;  // [batch] arrivals, then kGeoWords words: the split of the last attention launch
@@ -441,9 +443,15 @@ __device__ __forceinline__ int piece_count(int st, int en, int chunk) {
 // 8 output columns 8l..8l+7 and walks the pieces with the weights broadcast
 // by lane shuffles.  The first batch of partial loads is issued before the
 // lse arithmetic so a merge of a few pieces costs about one memory round trip.
+// A piece of weight 0 (lse = -inf) is selected out rather than multiplied, so
+// whatever its partial row holds (an empty shard's 0/0) cannot reach the sum;
+// a NaN lse (NaN inputs) gives a NaN weight and a NaN result.
+// With lse_dst, lane 0 also stores the merged natural-log sum-exp,
+// (M + log2 sum_i 2^(lse_i - M)) ln 2, or -inf when every piece is empty.
 template <class SlotFn>
 __device__ void merge_head_wave(const float* __restrict__ part_o, const float* __restrict__ part_lse, int S,
-                                SlotFn slot_of, float lse_mul, int h, uint16_t* __restrict__ out_head) {
+                                SlotFn slot_of, float lse_mul, int h, uint16_t* __restrict__ out_head,
+                                float* __restrict__ lse_dst) {
   const int lane = threadIdx.x & 63;
   constexpr int kBatch = 8;
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -475,8 +483,8 @@ __device__ void merge_head_wave(const float* __restrict__ part_o, const float* _
     for (int u = 0; u < kBatch; ++u)
       if (u < n) {
         const float wj = __shfl(wt, u);
-        acc0 += wj * a[u];
-        acc1 += wj * b[u];
+        acc0 += wj != 0.f ? wj * a[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1 += wj != 0.f ? wj * b[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     for (int j0 = kBatch; j0 < n; j0 += kBatch) {
 #pragma unroll
@@ -491,18 +499,19 @@ __device__ void merge_head_wave(const float* __restrict__ part_o, const float* _
       for (int u = 0; u < kBatch; ++u)
         if (j0 + u < n) {
           const float wj = __shfl(wt, j0 + u);
-          acc0 += wj * a[u];
-          acc1 += wj * b[u];
+          acc0 += wj != 0.f ? wj * a[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc1 += wj != 0.f ? wj * b[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
   }
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  const float inv = wsum == 0.f ? 0.f : 1.0f / wsum;
   u32x4_t pk;
   pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
   pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
   pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
   pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
   st_stream(pk, out_head + lane * 8);
+  if (lse_dst != nullptr && lane == 0) *lse_dst = wsum == 0.f ? -INFINITY : (M + fast_log2(wsum)) * kLn2;
 }
 
 // ------------------------------------------------------------- zero output
@@ -1067,9 +1076,15 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         st_stream(v, a.part_o + ((size_t)(pc.slot + q) * kHeads + h) * kVDim + kColsPerWave * w + c * 4);
       }
     }
-    if (!pc.complete && w == 0 && g == 0)
-      __builtin_nontemporal_store(Lsum > 0.f ? m_run[q] + fast_log2(Lsum) : -INFINITY,
-                                  &a.part_lse[(pc.slot + q) * kHeads + c16]);
+    if (w == 0 && g == 0) {
+      // no visible row: -inf (no weight in a merge); a NaN sum (NaN inputs) stays NaN so that it
+      // propagates through the merge as it does through an unsplit sequence
+      const float lse2 = Lsum == 0.f ? -INFINITY : m_run[q] + fast_log2(Lsum);
+      if (!pc.complete)
+        __builtin_nontemporal_store(lse2, &a.part_lse[(pc.slot + q) * kHeads + c16]);
+      else if (a.lse_out != nullptr)
+        a.lse_out[(size_t)t * kHeads + c16] = lse2 * kLn2;
+    }
   }
   __syncthreads();  // the shared tile and sums may be reused by the next piece
 }
@@ -1276,7 +1291,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
             const int h = w * (kHeads / kWaves) + hh;
             merge_head_wave(
                 a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i) * qmax + tau; }, 1.0f, h,
-                a.out + ((size_t)(t + tau) * kHeads + h) * kVDim);
+                a.out + ((size_t)(t + tau) * kHeads + h) * kVDim,
+                a.lse_out != nullptr ? a.lse_out + (size_t)(t + tau) * kHeads + h : nullptr);
           }
         if (threadIdx.x == 0) atomicExch(&a.counters[b], 0);
       }
@@ -1302,7 +1318,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
     int owner = (ipb - geo.base + geo.cost * j) / geo.chunk;
     if (owner > geo.n_wg - 1) owner = geo.n_wg - 1;
     if (owner == k)
-      for (int r = 0; r < (aux >> 16); ++r) zero_row_by_thread(a.out + (size_t)(qo + r) * kHeads * kVDim);
+      for (int r = 0; r < (aux >> 16); ++r) {
+        zero_row_by_thread(a.out + (size_t)(qo + r) * kHeads * kVDim);
+        if (a.lse_out != nullptr)
+          for (int h = 0; h < kHeads; ++h) a.lse_out[(size_t)(qo + r) * kHeads + h] = -INFINITY;
+      }
   }
 }
 
@@ -1340,19 +1360,21 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int qmax = a.max_q_len;
   merge_head_wave(
       a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i) * qmax + tau; }, 1.0f, h,
-      a.out + ((size_t)(qo + tau) * kHeads + h) * kVDim);
+      a.out + ((size_t)(qo + tau) * kHeads + h) * kVDim,
+      a.lse_out != nullptr ? a.lse_out + (size_t)(qo + tau) * kHeads + h : nullptr);
 }
 
 // Merge of caller-provided partials (natural-log lse), one wave per (sequence, head).
 __global__ __launch_bounds__(64) void mla_reduce_external_kernel(const float* part_o, const float* part_lse,
-                                                                 const int32_t* part_indptr, uint16_t* out) {
+                                                                 const int32_t* part_indptr, uint16_t* out,
+                                                                 float* lse_out) {
   const int b = blockIdx.x;
   const int h = blockIdx.y;
   const int p0 = part_indptr[b];
   const int S = part_indptr[b + 1] - p0;
   // S <= 0 leaves all weights zero and writes zeros
   merge_head_wave(part_o, part_lse, S < 0 ? 0 : S, [=](int i) { return p0 + i; }, kLog2e, h,
-                  out + ((size_t)b * kHeads + h) * kVDim);
+                  out + ((size_t)b * kHeads + h) * kVDim, lse_out != nullptr ? lse_out + (size_t)b * kHeads + h : nullptr);
 }
 
 // Streaming read probe (a diagnostic): workgroup k reads its own contiguous

@@ -42,7 +42,7 @@ def test_struct_layout_matches_header():
 
 
 def test_abi_version_and_status_strings():
-    assert B.mla_decode_abi_version() == 2
+    assert B.mla_decode_abi_version() == 3
     for code in range(5):
         s = B.mla_status_string(code)
         assert s.startswith("MLA_")
@@ -160,11 +160,39 @@ def test_run_rejects_bad_arguments_before_any_hip_call():
     assert run(unresolved) == B.MLA_ERR_INVALID_ARG
     # the two halves check the same things before any HIP call
     assert L.mla_decode_attend(ctypes.byref(plan), None, 4096, 4096, 4096, 4096, None, None, ok_scale, 1 / 24,
-                               4096, None) == B.MLA_ERR_INVALID_ARG
-    assert L.mla_decode_merge(ctypes.byref(plan), 4096, None, 4096, None) == B.MLA_ERR_INVALID_ARG
-    assert L.mla_decode_merge(None, 4096, 4096, 4096, None) == B.MLA_ERR_INVALID_ARG
-    assert L.mla_decode_merge(ctypes.byref(small), 4096, 4096, 4096, None) == B.MLA_ERR_WORKSPACE
+                               4096, None, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(ctypes.byref(plan), 4096, None, 4096, None, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(None, 4096, 4096, 4096, None, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(ctypes.byref(small), 4096, 4096, 4096, None, None) == B.MLA_ERR_WORKSPACE
     del ptrs
+
+
+def test_misaligned_pointers_are_rejected_before_any_launch():
+    # q, kv and out move in 16-byte pieces; indices, scales and lse_out are 4-byte words
+    L = B.lib()
+    plan = _fake_plan()
+    sc = 8192
+
+    def attend(q=4096, kv=4096, qo=4096, kvp=4096, idx=4096, last=None, qs=None, ks=sc, out=4096, lse=None):
+        return L.mla_decode_attend(ctypes.byref(plan), q, kv, qo, kvp, idx, last, qs, ks, 1 / 24, out, lse, None)
+
+    assert attend(q=4096 + 8) == B.MLA_ERR_INVALID_ARG
+    assert attend(kv=4096 + 4) == B.MLA_ERR_INVALID_ARG
+    assert attend(out=4096 + 2) == B.MLA_ERR_INVALID_ARG
+    assert attend(idx=4096 + 2) == B.MLA_ERR_INVALID_ARG
+    assert attend(qo=4096 + 1) == B.MLA_ERR_INVALID_ARG
+    assert attend(kvp=4096 + 3) == B.MLA_ERR_INVALID_ARG
+    assert attend(last=4096 + 2) == B.MLA_ERR_INVALID_ARG
+    assert attend(ks=sc + 1) == B.MLA_ERR_INVALID_ARG
+    assert attend(lse=8192 + 2) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(ctypes.byref(plan), 4096, 4096, 4096 + 8, None, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_merge(ctypes.byref(plan), 4096, 4096, 4096, 8192 + 1, None) == B.MLA_ERR_INVALID_ARG
+    R = L.mla_decode_reduce
+    assert R(4096 + 4, 4096, 4096, 2, 4096, None, None) == B.MLA_ERR_INVALID_ARG  # part_o
+    assert R(4096, 4096 + 2, 4096, 2, 4096, None, None) == B.MLA_ERR_INVALID_ARG  # part_lse
+    assert R(4096, 4096, 4096 + 2, 2, 4096, None, None) == B.MLA_ERR_INVALID_ARG  # part_indptr
+    assert R(4096, 4096, 4096, 2, 4096 + 8, None, None) == B.MLA_ERR_INVALID_ARG  # out
+    assert R(4096, 4096, 4096, 2, 4096, 8192 + 2, None) == B.MLA_ERR_INVALID_ARG  # lse_out
 
 
 def test_quantize_and_reduce_argument_checks():
@@ -183,9 +211,9 @@ def test_quantize_and_reduce_argument_checks():
     assert D(None, 1 << 20, 8192, 1 << 24, 1024, 10, None) == B.MLA_ERR_INVALID_ARG
     assert D(4096, 4100, 8192, 1 << 24, 1024, 10, None) == B.MLA_ERR_INVALID_ARG  # q overlaps its output
     assert D(4096, 1 << 20, 8192, (1 << 20) + 4, 1024, 10, None) == B.MLA_ERR_INVALID_ARG  # scratch overlaps
-    assert L.mla_decode_reduce(4096, 4096, 4096, 0, 4096, None) == B.MLA_ERR_INVALID_ARG
-    assert L.mla_decode_reduce(None, 4096, 4096, 2, 4096, None) == B.MLA_ERR_INVALID_ARG
-    assert L.mla_decode_reduce(4096, 4096, None, 2, 4096, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_reduce(4096, 4096, 4096, 0, 4096, None, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_reduce(None, 4096, 4096, 2, 4096, None, None) == B.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_reduce(4096, 4096, None, 2, 4096, None, None) == B.MLA_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")

@@ -264,26 +264,112 @@ def test_shared_and_repeated_pages(gpu, qd, kd):
 
 
 def test_external_reduce_matches_merge(gpu):
+    """The external reduce against the oracle's merge, output and final log-sum-exp.  Parts with lse = -inf
+    hold NaN rows (an empty shard's 0/0): they carry no weight and must not reach the output."""
     rng = np.random.default_rng(900)
-    counts = [0, 1, 2, 5, 64, 70, 3]
+    counts = [0, 1, 2, 5, 64, 70, 3, 2]
     P = sum(counts)
     part_o = rng.standard_normal((P, 16, 512)).astype(np.float32)
     lse = (rng.standard_normal((P, 16)) * 3).astype(np.float32)
     lse[1, 3] = -np.inf
     lse[rng.random((P, 16)) < 0.05] = -np.inf
+    lse[P - 2:, 5] = -np.inf  # the last sequence: head 5 has only empty parts
+    part_o[np.isneginf(lse)] = np.nan
     indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     out = torch.full((len(counts), 16, 512), float("nan"), dtype=torch.bfloat16, device=gpu)
+    lse_out = torch.full((len(counts), 16), float("nan"), dtype=torch.float32, device=gpu)
     binding.mla_decode_reduce(torch.from_numpy(part_o).to(gpu), torch.from_numpy(lse).to(gpu),
-                              torch.from_numpy(indptr).to(gpu), out)
+                              torch.from_numpy(indptr).to(gpu), out, lse_out)
     torch.cuda.synchronize()
     got = to64(out)
+    got_lse = lse_out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
     for b in range(len(counts)):
         p0, p1 = indptr[b], indptr[b + 1]
         if p1 == p0:
             assert np.array_equal(got[b], np.zeros((16, 512)))
+            assert np.all(np.isneginf(got_lse[b]))
             continue
-        ref = oracle.merge_partials(part_o[p0:p1].astype(np.float64), lse[p0:p1].astype(np.float64))
+        po = np.where(np.isneginf(lse[p0:p1])[:, :, None], 0.0, part_o[p0:p1].astype(np.float64))
+        ref = oracle.merge_partials(po, lse[p0:p1].astype(np.float64))
         assert np.max(np.abs(got[b] - ref)) <= 2.0 ** -8 * np.max(np.abs(ref)) + 1e-6, b
+        ref_lse = oracle.merge_lse(lse[p0:p1].astype(np.float64))
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isneginf(got_lse[b]), ~fin), b
+        assert np.max(np.abs(got_lse[b][fin] - ref_lse[fin]), initial=0.0) <= 1e-5 * (1 + np.max(np.abs(ref_lse[fin]), initial=0.0)), b
+    # without lse_out the output is the same
+    out2 = torch.empty_like(out)
+    binding.mla_decode_reduce(torch.from_numpy(part_o).to(gpu), torch.from_numpy(lse).to(gpu),
+                              torch.from_numpy(indptr).to(gpu), out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def _oracle_lse(case, sequences=None, causal=False, logit_cap=0.0):
+    q_bits = case.q_bits().numpy()
+    q_scale = None
+    if case.spec.q_dtype == "fp8":
+        q_bits, q_scale = oracle.bf16_bits_to_fp8_bits(q_bits), 1.0
+    kv_scale = float(case.kv_scale[0]) if case.kv_scale is not None else None
+    return oracle.mla_decode_lse(q_bits, case.kv_bits().numpy(), case.qo_indptr.numpy(), case.kv_indptr.numpy(),
+                                 case.kv_indices.numpy(), q_dtype=case.spec.q_dtype, kv_dtype=case.spec.kv_dtype,
+                                 q_scale=q_scale, kv_scale=kv_scale, sequences=sequences,
+                                 page_size=case.spec.page_size, kv_last_page_len=case.kv_last_page_len.numpy(),
+                                 causal=causal, logit_cap=logit_cap)
+
+
+def _check_lse(ref, got, what):
+    """Finite entries within 2e-3 absolute plus 1e-4 relative (the row sum uses bf16-rounded weights, each off by
+    at most 2^-9 relative, so log of the sum is off by at most ~2^-9; the max and the log add float32 rounding);
+    -inf exactly where the oracle has it."""
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: -inf pattern differs"
+    err = np.abs(got[fin] - ref[fin])
+    bound = 2e-3 + 1e-4 * np.abs(ref[fin])
+    log(f"  {what}: lse max_abs={err.max(initial=0.0):.3e}")
+    assert np.all(err <= bound), f"{what}: lse error {err.max()}"
+
+
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_final_lse_output(gpu, qd, kd):
+    """lse_out of mla_decode_run_paged: the natural-log sum-exp of every token and head, for sequences one
+    workgroup finishes, split ones (written by the merge), the fused merge and empty sequences."""
+    lens = [0, 1, 2, 31, 33, 100, 513, 2053, 0, 7]
+    spec = synth.CaseSpec(batch=len(lens), q_dtype=qd, kv_dtype=kd, lengths=lens, permuted=True,
+                          extra_pool_rows=17, seed=950 + PAIRS.index((qd, kd)))
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref_o = oracle_ref(case)
+    ref_l = _oracle_lse(case)
+    for units, chunk, flags in ((1, 32, 0), (8, 32, 0), (256, 32, 0), (256, 32, 1)):
+        dec = dc.decoder(num_units=units, min_chunk=chunk, flags=flags)
+        out = torch.full((case.total_q, 16, 512), float("nan"), dtype=torch.bfloat16, device=gpu)
+        lse = torch.full((case.total_q, 16), float("nan"), dtype=torch.float32, device=gpu)
+        dec.run(dc.q, dc.kv, dc.qo_indptr, dc.kv_indptr, dc.kv_indices, dc.q_scale, dc.kv_scale,
+                oracle.SM_SCALE, out, lse_out=lse)
+        torch.cuda.synchronize()
+        assert_parity(ref_o, to64(out), f"lse run {qd}/{kd} u{units} f{flags}")
+        _check_lse(ref_l, lse.cpu().numpy().astype(np.float64), f"{qd}/{kd} u{units} f{flags}")
+
+
+def test_final_lse_tokens_pages_and_cap(gpu):
+    lens = [3, 17, 1000, 4100, 64, 0]
+    q_lens = [2, 3, 1, 4, 2, 1]
+    spec = synth.CaseSpec(batch=len(lens), q_dtype="bf16", kv_dtype="fp8", lengths=lens, q_lens=q_lens,
+                          permuted=True, extra_pool_rows=40, page_size=16, seed=960)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    for causal, cap in ((True, 0.0), (False, 5.0), (True, 5.0)):
+        ref_l = _oracle_lse(case, causal=causal, logit_cap=cap)
+        for units in (8, 256):
+            dec = dc.decoder(num_units=units, min_chunk=32, logit_cap=cap,
+                             flags=binding.MLA_FLAG_CAUSAL if causal else 0)
+            out = torch.empty((case.total_q, 16, 512), dtype=torch.bfloat16, device=gpu)
+            lse = torch.full((case.total_q, 16), float("nan"), dtype=torch.float32, device=gpu)
+            dec.run(dc.q, dc.kv, dc.qo_indptr, dc.kv_indptr, dc.kv_indices, dc.q_scale, dc.kv_scale,
+                    oracle.SM_SCALE, out, kv_last_page_len=dc.kv_last_page_len, lse_out=lse)
+            torch.cuda.synchronize()
+            _check_lse(ref_l, lse.cpu().numpy().astype(np.float64), f"causal={causal} cap={cap} u{units}")
 
 
 def test_lengths_change_without_replanning(gpu):
