@@ -242,6 +242,31 @@ mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, co
                                 float sm_scale, void* out, float* lse_out, hipStream_t stream);
 
 /*
+ * mla_decode_run_paged for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no plan and no caller workspace.  The split partials and
+ * counters live in a library-owned array of MLA_NOALLOC_SCRATCH_BYTES in
+ * device memory, one per device, which that device holds until the process
+ * ends.  params are validated and resolved as mla_decode_plan does (against
+ * the current device; `stream` must belong to it); a problem whose
+ * workspace would exceed the array (mla_decode_workspace_size(params) >
+ * MLA_NOALLOC_SCRATCH_BYTES: e.g. more than 256 workgroup shares with one
+ * query token, or more than 128 with two) is MLA_ERR_WORKSPACE, before any
+ * launch.  The first call on a device looks up the array's device address
+ * (no allocation).  Every call on one device shares the array, so calls
+ * that may overlap in time on one device (two streams, two threads) race
+ * and must not be issued; calls in one stream are ordered.  With
+ * MLA_FLAG_FUSED_MERGE each call first clears the arrival counters with a
+ * small fill kernel.  Other arguments, layouts and errors as for
+ * mla_decode_run_paged.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (18u << 20)
+mla_status mla_decode_run_noalloc(const mla_decode_params* params, const void* q, const void* kv,
+                                  const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
+                                  float sm_scale, void* out, float* lse_out, hipStream_t stream);
+
+/*
  * Step a0 for fp8 queries: cast n bf16 values to fp8 e4m3fn with
  * round-to-nearest-even and no saturation (|x| > 464, +-inf and NaN become
  * the NaN code with the input's sign), as the pages cast Q straight to fp8

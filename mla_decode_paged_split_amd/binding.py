@@ -43,6 +43,8 @@ __all__ = [
     "mla_decode_quantize_q_dynamic",
     "MLA_QUANT_DYNAMIC_SCRATCH_BYTES",
     "mla_decode_reduce",
+    "mla_decode_run_noalloc",
+    "MLA_NOALLOC_SCRATCH_BYTES",
     "make_params",
     "Decoder",
 ]
@@ -58,6 +60,7 @@ MLA_FLAG_FUSED_MERGE = 1
 MLA_FLAG_FUSED_Q_CAST = 2
 MLA_FLAG_CAUSAL = 4
 MLA_QUANT_DYNAMIC_SCRATCH_BYTES = 1024
+MLA_NOALLOC_SCRATCH_BYTES = 18 << 20
 
 _DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3FN}
 
@@ -135,6 +138,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_quantize_q_dynamic.restype = ctypes.c_int
         L.mla_decode_reduce.argtypes = [vp, vp, vp, i32, vp, vp, vp]
         L.mla_decode_reduce.restype = ctypes.c_int
+        L.mla_decode_run_noalloc.argtypes = [ctypes.POINTER(MlaDecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, f32,
+                                             vp, vp, vp]
+        L.mla_decode_run_noalloc.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -294,6 +300,19 @@ def mla_decode_reduce(part_o: torch.Tensor, part_lse: torch.Tensor, part_indptr:
     code = lib().mla_decode_reduce(_ptr(part_o), _ptr(part_lse), _ptr(part_indptr), batch, _ptr(out),
                                    _ptr(lse_out), _stream(stream))
     _check(code, "mla_decode_reduce")
+
+
+def mla_decode_run_noalloc(params: MlaDecodeParams, q: torch.Tensor, kv: torch.Tensor, qo_indptr: torch.Tensor,
+                           kv_indptr: torch.Tensor, kv_indices: torch.Tensor, kv_last_page_len: Optional[torch.Tensor],
+                           q_scale: Optional[torch.Tensor], kv_scale: Optional[torch.Tensor], sm_scale: float,
+                           out: torch.Tensor, lse_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode step with the library's own scratch array as the workspace (no plan, no allocation)."""
+    _check_index_args(out, lse_out, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                      kv_last_page_len=kv_last_page_len)
+    code = lib().mla_decode_run_noalloc(ctypes.byref(params), _ptr(q), _ptr(kv), _ptr(qo_indptr), _ptr(kv_indptr),
+                                        _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(q_scale), _ptr(kv_scale),
+                                        float(sm_scale), _ptr(out), _ptr(lse_out), _stream(stream))
+    _check(code, "mla_decode_run_noalloc")
 
 
 class Decoder:

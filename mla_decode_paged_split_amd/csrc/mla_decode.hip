@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mla_decode.h"
 #include "mla_device.hpp"
 
@@ -178,6 +180,28 @@ mla_status make_args(const mla_decode_plan_t* plan, const int32_t* qo_indptr, co
   return MLA_OK;
 }
 
+// Workspace of mla_decode_run_noalloc: one copy per device, reached only
+// through the address hipGetSymbolAddress reports for that device (in host
+// code the array's name is not a device address).
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, looked up on the first call there
+
+// The device address of `scratch` on `device` (the current device).
+mla_status scratch_on(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MLA_ERR_HIP;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -310,6 +334,52 @@ mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, co
                                     kv_scale, sm_scale, out, lse_out, stream);
   if (st != MLA_OK) return st;
   return mla_decode_merge(plan, qo_indptr, kv_indptr, out, lse_out, stream);
+}
+
+mla_status mla_decode_run_noalloc(const mla_decode_params* params, const void* q, const void* kv,
+                                  const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,
+                                  float sm_scale, void* out, float* lse_out, hipStream_t stream) {
+  mla_status st = validate_params(params);
+  if (st != MLA_OK) return st;
+  // the sizes that do not need the device are checked before any HIP call
+  if (params->num_units > 0 && layout_for(params, params->num_units).total > MLA_NOALLOC_SCRATCH_BYTES)
+    return MLA_ERR_WORKSPACE;
+  int32_t units = 0, device = 0;
+  st = resolve_units(params, &units, &device);
+  if (st != MLA_OK) return st;
+  const Layout L = layout_for(params, units);
+  if (L.total > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  int32_t sdev = 0;
+  st = stream_device(stream, &sdev);
+  if (st != MLA_OK) return st;
+  if (sdev != device) return MLA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  st = scratch_on(device, &ws);
+  if (st != MLA_OK) return st;
+
+  mla_decode_plan_t pl;
+  memset(&pl, 0, sizeof(pl));
+  pl.params = *params;
+  pl.params.num_units = units;
+  pl.params.min_chunk = params->min_chunk > 0 ? params->min_chunk : kDefaultMinChunk;
+  pl.params.max_q_len = max_q_of(params);
+  pl.workspace = ws;
+  pl.workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  pl.device = device;
+  pl.off_counters = L.counters;
+  pl.off_part_o = L.part_o;
+  pl.off_part_lse = L.part_lse;
+  if (params->flags & MLA_FLAG_FUSED_MERGE) {
+    // arrival counters must start at zero; an earlier call with another batch may have left its split
+    // record where this call's counters are
+    int32_t* counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.counters);
+    const int n = params->batch;
+    hipLaunchKernelGGL(mla::mla_fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, counters, n, 0);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  }
+  return mla_decode_run_paged(&pl, q, kv, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_scale, kv_scale,
+                              sm_scale, out, lse_out, stream);
 }
 
 mla_status mla_decode_run(const mla_decode_plan_t* plan, const void* q, const void* kv, const int32_t* qo_indptr,
