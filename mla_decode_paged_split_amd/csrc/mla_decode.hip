@@ -111,7 +111,7 @@ int ilog2(int v) {
 // sequence table read the indptrs from memory.
 template <mla::Dt QT, mla::Dt KT, int QL, int kForm>
 hipError_t launch_attention_ql(const mla::Args& a, hipStream_t stream) {
-  if (a.batch <= mla::kSeqTable)
+  if (a.batch <= mla::seq_table<KT, QL>())
     hipLaunchKernelGGL((mla::mla_decode_kernel<QT, KT, false, QL, kForm>), dim3(a.units), dim3(mla::kThreads), 0,
                        stream, a);
   else

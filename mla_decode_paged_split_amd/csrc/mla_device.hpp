@@ -54,8 +54,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTileRows = 64;             // KV rows per workgroup tile: 16 per wave
 constexpr int kColsPerWave = kVDim / kWaves;  // 128 output columns per wave
 constexpr int kSplitAlign = 32;           // share sizes are multiples of this
-constexpr int kScanPerThread = 4;         // sequences each thread reads in the first round trip
-constexpr int kSeqTable = kScanPerThread * kThreads;  // sequences whose indptr values are kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;     // log2 growth of the running max tolerated before rescaling
@@ -94,38 +92,91 @@ struct KvLayout<Dt::BF16> {
 };
 
 
-// Q of a pass staged once per workgroup (fp8 KV only; bf16 KV leaves no LDS
-// for it): one row per token and head, bf16 (1152 B) or fp8 (576 B) values,
-// rows padded to 1168 B.
+// Q of a pass staged once per workgroup (fp8 KV only; bf16 KV keeps Q in
+// each wave's registers): one row per token and head, bf16 (1152 B) or fp8
+// (576 B) values, rows padded to 1168 B.
 constexpr int kQPitch = 1168;
-template <Dt KV, int QL>
-constexpr int q_stage_rows() {
-  return KV == Dt::FP8 ? QL * kHeads : 1;
-}
 
-// Output staging at the finish, per wave and token, inside the V buffers: 16
-// head rows of the wave's 128 columns, float32 (512 bytes) or bf16 (256
+// Output staging at the finish, per wave and token, inside the tile buffers:
+// 16 head rows of the wave's 128 columns, float32 (512 bytes) or bf16 (256
 // bytes), each row padded by 16 bytes so that rows land on different banks.
 constexpr int kOutPitchF32 = kColsPerWave * 4 + 16;
 constexpr int kOutPitchBf16 = kColsPerWave * 2 + 16;
 constexpr int kOutStageBytes = kHeads * kOutPitchF32;
 
+// Two ways to stream the KV rows.  fp8 KV with one token per pass sends whole
+// tiles into a ring of kSlots LDS tiles with direct-to-LDS loads: a tile is
+// read by S^T in one step and by P.V in the next, so two of the four slots
+// are in use and two tiles are in flight.  bf16 KV, and fp8 KV with two
+// tokens per pass (whose second token's Q and accumulators leave no registers
+// for the LDS ring's operands), hold the rows in a register ring and copy
+// each tile's V part into one of two LDS buffers for P.V.
 template <Dt KV, int QL>
-struct alignas(16) Smem {
-  uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];  // V part of the current / next tile
-  uint8_t q[q_stage_rows<KV, QL>()][kQPitch];       // the pass's Q (fp8 KV)
+constexpr bool lds_ring() {
+  return KV == Dt::FP8 && QL == 1;
+}
+constexpr int kSlots = 4;
+constexpr int kF8Row = 576;
+
+// Sequences each thread reads in the first round trip, and the LDS table of
+// their indptr values (what is left of the LDS beside the tile buffers).
+template <Dt KV, int QL>
+constexpr int scan_per_thread() {
+  return lds_ring<KV, QL>() ? 2 : 4;
+}
+template <Dt KV, int QL>
+constexpr int seq_table() {
+  return scan_per_thread<KV, QL>() * kThreads;
+}
+
+template <Dt KV, int QL, bool kLds = lds_ring<KV, QL>()>
+struct Smem;
+
+// Register ring: the V parts of the current and the next tile, and the
+// pass's Q (fp8 KV only; bf16 KV keeps Q in each wave's registers).
+template <Dt KV, int QL>
+struct alignas(16) Smem<KV, QL, false> {
+  uint8_t v[2][kTileRows][KvLayout<KV>::kVPitch];
+  uint8_t q[KV == Dt::FP8 ? QL * kHeads : 1][kQPitch];
   u32x2_t p[2][QL][kWaves][64];     // bf16 weights: token, wave, lane -> 4 rows of one head
   float mx[2][kWaves][QL][kHeads];  // per-wave tile max of each token and head
   float lsum[kWaves][QL][kHeads];
-  int seq[kSeqTable][4];  // kv_indptr[b], kv_indptr[b+1], qo_indptr[b], (tokens << 16) | last-page rows
-                          // of the first kSeqTable sequences
+  int seq[seq_table<KV, QL>()][4];  // kv_indptr[b], kv_indptr[b+1], qo_indptr[b],
+                                    // (tokens << 16) | last-page rows of the first sequences
   int differs[kWaves];  // per wave: some sequence's length differs from the first's
   int bmin;
   int bmax;
   int arrive;
+  __device__ uint8_t* out_stage() { return &v[0][0][0]; }
+  __device__ uint8_t* q_stage() { return &q[0][0]; }
 };
-static_assert(sizeof(((Smem<Dt::FP8, 1>*)nullptr)->v) >= (size_t)kWaves * kOutStageBytes, "output staging fits the V buffers");
-static_assert(sizeof(((Smem<Dt::BF16, 1>*)nullptr)->v) >= (size_t)kWaves * kOutStageBytes, "output staging fits the V buffers");
+
+// LDS ring: whole tiles (64 rows of 576 B).  Row R of a tile is at byte
+// R * 576 of its slot and holds its 16-byte chunk c at position kpos(R, c),
+// which spreads the fragment reads over the banks.  The pass's Q is staged in
+// the last slot before that slot's first tile is loaded.
+template <Dt KV, int QL>
+struct alignas(16) Smem<KV, QL, true> {
+  static_assert(KV == Dt::FP8 && QL == 1, "the LDS ring holds fp8 tiles for one token");
+  uint8_t k[kSlots][kTileRows][kF8Row];
+  u32x2_t p[2][QL][kWaves][64];
+  float mx[2][kWaves][QL][kHeads];
+  float lsum[kWaves][QL][kHeads];
+  int seq[seq_table<KV, QL>()][4];
+  int differs[kWaves];
+  int bmin;
+  int bmax;
+  int arrive;
+  __device__ uint8_t* out_stage() { return &k[0][0][0]; }
+  __device__ uint8_t* q_stage() { return &k[kSlots - 1][0][0]; }
+};
+static_assert(sizeof(((Smem<Dt::BF16, 1>*)nullptr)->v) >= (size_t)kWaves * kOutStageBytes, "output staging fits");
+static_assert(sizeof(((Smem<Dt::FP8, 2>*)nullptr)->v) >= (size_t)kWaves * kOutStageBytes, "output staging fits");
+static_assert(sizeof(((Smem<Dt::FP8, 1>*)nullptr)->k[0]) >= (size_t)kWaves * kOutStageBytes, "output staging fits");
+static_assert(sizeof(((Smem<Dt::FP8, 1>*)nullptr)->k[0]) >= (size_t)kHeads * kQPitch, "one token's Q fits a slot");
+static_assert(sizeof(Smem<Dt::FP8, 1>) <= 160 * 1024 && sizeof(Smem<Dt::FP8, 2>) <= 160 * 1024 &&
+                  sizeof(Smem<Dt::BF16, 1>) <= 160 * 1024,
+              "LDS of one workgroup");
 
 struct Args {
   const void* q;
@@ -557,10 +608,108 @@ constexpr int ring_depth() {
 template <Dt KT, int Depth>
 struct Ring {
   static constexpr int D = Depth;
+  static constexpr bool kNext = true;
   u32x4_t dat[D][KvLayout<KT>::kChunks];
   int first[D];  // pages of tiles 0..D-1
   int next[D];   // pages of tiles D..2D-1, then of each slot's next refill
 };
+
+// fp8 KV: the page index of the tile each LDS slot receives next (tile t
+// goes to slot t % kSlots).  first / next hold tiles 0..3 and 4..7 when a
+// piece starts; after the first three tiles are requested, slot j's entry is
+// the next tile it receives.
+struct LdsRing {
+  static constexpr int D = kSlots;
+  static constexpr bool kNext = false;  // the pages of tiles 4..6 are loaded as tiles 0..2 go out
+  int first[D];
+};
+
+template <Dt QT, Dt KT, int QL>
+using RingOf = std::conditional_t<lds_ring<KT, QL>(), LdsRing, Ring<KT, ring_depth<QT, KT, QL>()>>;
+
+// Position of chunk c of tile row R inside its row.  With a = (R >> 2) & 3,
+// the chunk index is xor-ed with a, and for the 32 V chunks also with
+// (a & 1) << 3 (a 128-byte move that keeps them inside the first 32).  An
+// S^T fragment read (16 rows, one chunk each) then hits 16 different
+// 16-byte bank groups, and a P.V read (rows 4 apart, 128 contiguous bytes
+// each) puts the two 16-lane groups served together 128 bytes apart.  The
+// map is its own inverse on each row.
+__device__ __forceinline__ int kpos(int R, int c) {
+  const int a = (R >> 2) & 3;
+  return c ^ a ^ (c < 32 ? (a & 1) << 3 : 0);
+}
+
+// Direct-to-LDS loads of this wave's 16 rows of a tile into `slot`: tile
+// row R = 16w + r goes to slot + R * 576, chunk c of it to position
+// kpos(R, c) (kpos(16w + r, c) == kpos(r, c)).  The wave's rows are 576 sixteen-byte units of the slot;
+// instruction i fills units 64i .. 64i + 63 (lane l unit 64i + l), so each
+// instruction writes 1 KB of LDS and, for rows that are neighbours in the
+// pool, reads 1 KB of contiguous memory: whole lines, with the non-temporal
+// hint so nothing lingers in the caches.  Every lane of every instruction
+// is active (an exec-masked block would make the compiler assume it may be
+// skipped and drain every load in flight where it waits for the page
+// indices).  Lane l's row of instruction i is fetched from the lane that
+// holds it (row_v: lane r < 16 holds the pool row of the wave's row r) with
+// ds_bpermute; the per-lane source lane and chunk offset are constants.
+struct DmaLanes {
+  int src[9];       // ds_bpermute byte address of the lane holding this lane's row
+  uint32_t off[9];  // byte offset of this lane's chunk in its row
+};
+
+__device__ __forceinline__ DmaLanes dma_lanes() {
+  DmaLanes d;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int u = 64 * i + lane;
+    const int r = u / 36;
+    d.src[i] = r * 4;
+    d.off[i] = (uint32_t)(kpos(r, u - r * 36) << 4);  // the chunk stored at this position
+  }
+  return d;
+}
+
+// The rows of the 9 instructions, fetched ahead of the loads (the exchange
+// goes through the LDS unit; fetched well before the loads, its latency is
+// hidden and the loads need no wait of their own).
+struct DmaRows {
+  uint32_t row[9];
+};
+__device__ __forceinline__ DmaRows dma_rows(int row_v, const DmaLanes& dl) {
+  DmaRows r;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) r.row[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(dl.src[i], row_v);
+  return r;
+}
+// Instruction i of a tile's loads; `dst` is this wave's 16 rows of the slot.
+__device__ __forceinline__ void dma_one(const void* kv, uint8_t* dst, const DmaRows& r, const DmaLanes& dl, int i) {
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(kv) + (size_t)r.row[i] * kF8Row + dl.off[i];
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                   reinterpret_cast<__attribute__((address_space(3))) void*>((uintptr_t)(dst + i * 1024)),
+                                   16, 0, 2 /* nt */);
+}
+__device__ __forceinline__ void dma_issue(const void* kv, uint8_t* dst, const DmaRows& r, const DmaLanes& dl) {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) dma_one(kv, dst, r, dl, i);
+}
+// Vector-memory instructions per tile: its 9 loads, then one page-index load
+// (of the tile 4 later into the same slot).  Every tile, the first ones
+// included, is issued in this pattern, so one wait count serves every step.
+constexpr int kDmaOps = 9;
+constexpr int kTileOps = kDmaOps + 1;
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (the direct-to-LDS loads land in LDS when they leave this count).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits for this wave's LDS operations but not for
+// its direct-to-LDS loads in flight (__syncthreads would: they write LDS).
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Fetch the ring's starting page indices for a piece of nrows rows beginning
 // at index position ip0.
@@ -571,8 +720,10 @@ __device__ __forceinline__ void issue_ring_indices(const int32_t* __restrict__ k
   const int my_row = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15);
 #pragma unroll
   for (int k = 0; k < D; ++k) r.first[k] = piece_page(kv_indices, ip0, nrows, k * kTileRows + my_row, sh);
+  if constexpr (R::kNext) {
 #pragma unroll
-  for (int k = 0; k < D; ++k) r.next[k] = piece_page(kv_indices, ip0, nrows, (k + D) * kTileRows + my_row, sh);
+    for (int k = 0; k < D; ++k) r.next[k] = piece_page(kv_indices, ip0, nrows, (k + D) * kTileRows + my_row, sh);
+  }
 }
 
 // Start the loads of the ring's first D tiles (in the steady state's slot
@@ -644,11 +795,21 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
                              float out_mul, RingT& ring) {
   using L = KvLayout<KT>;
   constexpr int D = RingT::D;
+  constexpr bool kLds = lds_ring<KT, QL>();
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int g = lane >> 4;
   const int sh = kGeneral ? a.page_shift : 0;
+  const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
+  // LDS ring: the per-lane constants of the tile loads, the rows of the tile
+  // whose loads the next step issues, this wave's 16 rows in a slot (the wave
+  // index made a scalar once) and the next S^T's K fragments
+  [[maybe_unused]] DmaLanes dl;
+  if constexpr (kLds) dl = dma_lanes();
+  [[maybe_unused]] DmaRows pend;
+  [[maybe_unused]] const int wrow_bytes = 16 * __builtin_amdgcn_readfirstlane(w) * kF8Row;
+  [[maybe_unused]] u32x4_t kcur[KvLayout<KT>::kChunks];
 
   // Q as the B operand of S^T = K . Q^T (lane holds head c16).  A k-step takes
   // 8 values per lane; for fp8 KV a 16-byte chunk feeds two k-steps, for bf16
@@ -660,9 +821,10 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   if constexpr (KT == Dt::FP8) {
     // Q goes through LDS: the workgroup loads each token's 16 rows once (16-byte
     // pieces over all 256 threads) instead of every wave loading all of them,
-    // so 4x fewer requests sit in front of the ring's rows.  Order: Q loads,
-    // the ring's rows, then Q into LDS (cast to fp8 there when fp8 Q is given
-    // as bf16), a barrier, and each wave's fragments from LDS.
+    // so 4x fewer requests sit in front of the tiles.  Order: Q loads, the
+    // first three tiles (slots 0..2), then Q into LDS slot 3 (cast to fp8
+    // there when fp8 Q is given as bf16), a barrier once tile 0 has landed,
+    // and each wave's fragments from LDS.
     const bool src16 = (QT == Dt::BF16) || a.q_cast;  // the source holds bf16 values
     constexpr int kChunks16 = kHeads * kQKDim * 2 / 16;  // 1152 sixteen-byte pieces of a bf16 Q token
     constexpr int kPer = (kChunks16 + kThreads - 1) / kThreads;  // 5
@@ -684,7 +846,21 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         stage[q][i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)c * 16);
       }
     }
-    issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
+    if constexpr (kLds) {
+      // tiles 0 and 1 now (ring.first[j] becomes the page of the next tile
+      // slot j receives: 4 and 5); tile 2 goes out during the first step's
+      // S^T, as every later tile goes out during the S^T of the step after
+      // the one that freed its slot
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        dma_issue(a.kv, &sm.k[k][0][0] + wrow_bytes,
+                  dma_rows(page_row(ring.first[k], pc.nrows, k * kTileRows + my_row, sh), dl), dl);
+        ring.first[k] = piece_page(a.kv_indices, pc.ip0, pc.nrows, (k + kSlots) * kTileRows + my_row, sh);
+      }
+      pend = dma_rows(page_row(ring.first[2], pc.nrows, 2 * kTileRows + my_row, sh), dl);
+    } else {
+      issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
+    }
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
 #pragma unroll
@@ -693,7 +869,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         if (c < nchunks) {
           const int h = c / per_head;
           const int off = (c - h * per_head) * 16;  // byte offset in the source row
-          uint8_t* dst = &sm.q[q * kHeads + h][0];
+          uint8_t* dst = sm.q_stage() + (q * kHeads + h) * kQPitch;
           if (QT == Dt::FP8 && a.q_cast)
             *reinterpret_cast<uint64_t*>(dst + off / 2) = bf16x8_to_e4m3fn(stage[q][i]);
           else
@@ -701,10 +877,15 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         }
       }
     }
-    __syncthreads();
+    if constexpr (kLds) {
+      wait_vm<kTileOps + 1>();  // tile 0 is in LDS (after it: tile 1's loads and two page loads)
+      lds_barrier();
+    } else {
+      __syncthreads();
+    }
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
-      const uint8_t* row = &sm.q[q * kHeads + c16][0];
+      const uint8_t* row = sm.q_stage() + (q * kHeads + c16) * kQPitch;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         const int d0 = ((s >> 1) * 4 + g) * 16 + (s & 1) * 8;
@@ -733,13 +914,22 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
 #pragma unroll
   for (int q = 0; q < QL; ++q) maxlim = max(maxlim, pc.lim[q]);
   const int T = (maxlim + kTileRows - 1) / kTileRows;
-  const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
 
-  // the ring is primed: tiles 0..D-1 in flight, pages of D..2D-1 loaded
-  auto& dat = ring.dat;
-  auto& idxn = ring.next;
+  // the ring is primed: tiles 0..D-1 in flight (fp8 KV: 0..2 in flight, tile 0
+  // in LDS), pages of the next ones loaded
   auto page_index = [&](int tt) { return piece_page(a.kv_indices, pc.ip0, pc.nrows, tt * kTileRows + my_row, sh); };
+  // fp8 KV: the K fragments of the tile in slot `sl`: lane (c16, g) reads chunks 4j + g of row
+  // 16w + c16 (kpos(16w + c16, .) == kpos(c16, .))
+  auto read_k = [&](int sl) {
+    if constexpr (kLds) {
+      const uint8_t* krow = &sm.k[sl][0][0] + my_row * kF8Row;
+#pragma unroll
+      for (int j = 0; j < L::kChunks; ++j)
+        kcur[j] = *reinterpret_cast<const u32x4_t*>(krow + (kpos(c16, 4 * j + g) << 4));
+    }
+  };
+  read_k(0);  // LDS ring: tile 0 is complete since the start's barrier
   // this lane's first 16-byte chunk of its row of tile tt (the row's chunks j are 64 bytes apart)
   auto tile_src = [&](int page, int tt) {
     const int row = page_row(page, pc.nrows, tt * kTileRows + my_row, sh);
@@ -762,6 +952,38 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // k-step ks covers rows 32ks..32ks+31; slot s of lane group g is row
   // R = 32ks + (s/4)*16 + g*4 + s%4, which is wave 2ks + s/4's row g*4 + s%4.
   // Block jb holds columns 128w + m*8 + jb, m = 0..15; lane c16 feeds m = c16.
+  // LDS ring: the next P.V's operands, read from LDS right after the barrier
+  // that publishes them (V of the tile, still in its slot; its weights), so
+  // that the next step's products wait for no LDS read
+  [[maybe_unused]] u32x2_t vreg[2][8];
+  [[maybe_unused]] u32x2_t preg[QL][2][2];
+  // V of tile tt: columns 128w + 8 c16 .. + 7 of row R lie in chunk 8w + c16 / 2,
+  // half c16 & 1; these rows have (R >> 2) & 3 == g, so the chunk sits at kpos(4g, 8w + c16 / 2)
+  auto load_v = [&](int tt) {
+    if constexpr (kLds) {
+      const uint8_t* vt = &sm.k[tt & (kSlots - 1)][0][0];
+      const int vcol = (kpos(4 * g, 8 * w + (c16 >> 1)) << 4) + ((c16 & 1) << 3);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int R = 32 * ks + (sl >> 2) * 16 + g * 4 + (sl & 3);
+          vreg[ks][sl] = *reinterpret_cast<const u32x2_t*>(vt + R * kF8Row + vcol);
+        }
+    }
+  };
+  auto load_p = [&](int tt) {
+    if constexpr (kLds) {
+#pragma unroll
+      for (int q = 0; q < QL; ++q)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          preg[q][ks][0] = sm.p[tt & 1][q][2 * ks][lane];
+          preg[q][ks][1] = sm.p[tt & 1][q][2 * ks + 1][lane];
+        }
+    }
+  };
+
   auto pv = [&](int tt) {
     const int buf = tt & 1;
 #pragma unroll
@@ -770,8 +992,14 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
 #pragma unroll
       for (int q = 0; q < QL; ++q) {
         u32x4_t pp;
-        const u32x2_t p0 = sm.p[buf][q][2 * ks][lane];
-        const u32x2_t p1 = sm.p[buf][q][2 * ks + 1][lane];
+        u32x2_t p0, p1;
+        if constexpr (kLds) {
+          p0 = preg[q][ks][0];
+          p1 = preg[q][ks][1];
+        } else {
+          p0 = sm.p[buf][q][2 * ks][lane];
+          p1 = sm.p[buf][q][2 * ks + 1][lane];
+        }
         pp[0] = p0[0];
         pp[1] = p0[1];
         pp[2] = p1[0];
@@ -780,10 +1008,15 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       }
       if constexpr (KT == Dt::FP8) {
         u32x2_t rv[8];
+        if constexpr (kLds) {
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int R = 32 * ks + (sl >> 2) * 16 + g * 4 + (sl & 3);
-          rv[sl] = *reinterpret_cast<const u32x2_t*>(&sm.v[buf][R][kColsPerWave * w + c16 * 8]);
+          for (int sl = 0; sl < 8; ++sl) rv[sl] = vreg[ks][sl];
+        } else {
+#pragma unroll
+          for (int sl = 0; sl < 8; ++sl) {
+            const int R = 32 * ks + (sl >> 2) * 16 + g * 4 + (sl & 3);
+            rv[sl] = *reinterpret_cast<const u32x2_t*>(&sm.v[buf][R][kColsPerWave * w + c16 * 8]);
+          }
         }
 #pragma unroll
         for (int wd = 0; wd < 2; ++wd) {
@@ -837,7 +1070,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // between the same two barriers; the weights of tile tt are made with the
   // running max known before it and kept unless some score of the tile exceeds
   // that max by more than the slack (then every wave rescales and redoes them).
-  auto step = [&](auto kc, int tt, auto refill) {
+  auto step = [&](auto kc, int tt, auto refill, auto pend_in) {
     constexpr int k = decltype(kc)::value;
     const int buf = tt & 1;
     // ---- S^T for this wave's 16 rows and each token (two accumulation chains); V part to LDS
@@ -847,65 +1080,114 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       s0[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       s1[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    uint8_t* vrow = &sm.v[buf][16 * w + c16][0];
-    // The slot is refilled with tile tt + D chunk by chunk, each load issued
-    // right after its chunk is used (rows past the piece clamp to its first
-    // row, so every steady-state trip issues the same loads and the compiler's
-    // wait counts stay exact).  Spread over the products, the four waves' loads
-    // reach the address unit a few at a time instead of as one burst of 36 that
-    // would hold each wave for most of a tile.
-    // The index of tile tt + 2D goes out before these refills, so the next
-    // use of the slot waits for it without waiting for all of its tile.
-    const uint8_t* nsrc = nullptr;
-    if constexpr (decltype(refill)::value) {
-      nsrc = tile_src(idxn[k], tt + D);
-      idxn[k] = page_index(tt + 2 * D);
+    // LDS ring: the rows of tile tt + 3 (its slot, tile tt - 1's, frees at
+    // this step's barrier; its loads go out during the next step's S^T),
+    // exchanged now so that the loads need no wait
+    [[maybe_unused]] DmaRows next_rows;
+    if constexpr (kLds && decltype(refill)::value) {
+      constexpr int sl = (k + kSlots - 1) % kSlots;
+      next_rows = dma_rows(page_row(ring.first[sl], pc.nrows, (tt + kSlots - 1) * kTileRows + my_row, sh), dl);
     }
-    // bf16 Q over fp8 K: chunk j + 1 is widened while chunk j's products run
-    // (the fences around each refill would otherwise keep them apart)
-    bf16x8_t wk0, wk1;
-    if constexpr (QT == Dt::BF16 && KT == Dt::FP8) {
-      wk0 = fp8x8_to_bf16x8(dat[k][0][0], dat[k][0][1]);
-      wk1 = fp8x8_to_bf16x8(dat[k][0][2], dat[k][0][3]);
-    }
+    if constexpr (kLds) {
+      // K fragments of tile tt: read from its slot right after the barrier
+      // that made it complete (the previous step's, or the start's), so the
+      // products start at once
+      const u32x4_t (&kk)[L::kChunks] = kcur;
+      // tile tt + 2's loads (pending since the last barrier) go out one per
+      // chunk, between the products: the four waves' 36 loads then reach the
+      // address unit spread over the step instead of as one burst after the
+      // barrier, which held every wave for ~460 cycles
+      uint8_t* pslot = &sm.k[(k + 2) % kSlots][0][0] + wrow_bytes;
 #pragma unroll
-    for (int j = 0; j < L::kChunks; ++j) {
-      const u32x4_t kk = dat[k][j];
-      if (j < L::kVChunks) *reinterpret_cast<u32x4_t*>(vrow + (j * 4 + g) * 16) = kk;
-      if constexpr (KT == Dt::BF16) {
-        const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kk);
-#pragma unroll
-        for (int q = 0; q < QL; ++q) {
-          if (j & 1)
-            s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[q][j], s1[q], 0, 0, 0);
-          else
-            s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[q][j], s0[q], 0, 0, 0);
+      for (int j = 0; j < L::kChunks; ++j) {
+        if constexpr (decltype(pend_in)::value) {
+          __builtin_amdgcn_sched_barrier(0);
+          dma_one(a.kv, pslot, pend, dl, j);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      } else if constexpr (QT == Dt::BF16) {
-        const bf16x8_t k0 = wk0;
-        const bf16x8_t k1 = wk1;
-        if (j + 1 < L::kChunks) {
-          wk0 = fp8x8_to_bf16x8(dat[k][j + 1][0], dat[k][j + 1][1]);
-          wk1 = fp8x8_to_bf16x8(dat[k][j + 1][2], dat[k][j + 1][3]);
-        }
+        if constexpr (QT == Dt::BF16) {
+          // bf16 Q over fp8 K: the fp8 values widen to bf16 exactly
+          const bf16x8_t k0 = fp8x8_to_bf16x8(kk[j][0], kk[j][1]);
+          const bf16x8_t k1 = fp8x8_to_bf16x8(kk[j][2], kk[j][3]);
 #pragma unroll
-        for (int q = 0; q < QL; ++q) {
-          s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[q][2 * j], s0[q], 0, 0, 0);
-          s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[q][2 * j + 1], s1[q], 0, 0, 0);
-        }
-      } else {
-        const uint64_t k0 = (uint64_t)kk[0] | ((uint64_t)kk[1] << 32);
-        const uint64_t k1 = (uint64_t)kk[2] | ((uint64_t)kk[3] << 32);
+          for (int q = 0; q < QL; ++q) {
+            s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[q][2 * j], s0[q], 0, 0, 0);
+            s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[q][2 * j + 1], s1[q], 0, 0, 0);
+          }
+        } else {
+          const uint64_t k0 = (uint64_t)kk[j][0] | ((uint64_t)kk[j][1] << 32);
+          const uint64_t k1 = (uint64_t)kk[j][2] | ((uint64_t)kk[j][3] << 32);
 #pragma unroll
-        for (int q = 0; q < QL; ++q) {
-          s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k0, (long)q8[q][2 * j], s0[q], 0, 0, 0);
-          s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k1, (long)q8[q][2 * j + 1], s1[q], 0, 0, 0);
+          for (int q = 0; q < QL; ++q) {
+            s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k0, (long)q8[q][2 * j], s0[q], 0, 0, 0);
+            s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k1, (long)q8[q][2 * j + 1], s1[q], 0, 0, 0);
+          }
         }
       }
+      // the page of the tile this slot receives after tile tt + 2
+      if constexpr (decltype(pend_in)::value) ring.first[(k + 2) % kSlots] = page_index(tt + 2 * kSlots - 2);
+    } else {
+      auto& dat = ring.dat;
+      auto& idxn = ring.next;
+      uint8_t* vrow = &sm.v[buf][16 * w + c16][0];
+      // The slot is refilled with tile tt + D chunk by chunk, each load issued
+      // right after its chunk is used (rows past the piece clamp to its first
+      // row, so every steady-state trip issues the same loads and the compiler's
+      // wait counts stay exact).  Spread over the products, the four waves' loads
+      // reach the address unit a few at a time instead of as one burst.
+      // The index of tile tt + 2D goes out before these refills, so the next
+      // use of the slot waits for it without waiting for all of its tile.
+      const uint8_t* nsrc = nullptr;
       if constexpr (decltype(refill)::value) {
-        __builtin_amdgcn_sched_barrier(0);
-        dat[k][j] = *reinterpret_cast<const u32x4_t*>(nsrc + j * 64);
-        __builtin_amdgcn_sched_barrier(0);
+        nsrc = tile_src(idxn[k], tt + D);
+        idxn[k] = page_index(tt + 2 * D);
+      }
+      // bf16 Q over fp8 K: chunk j + 1 is widened while chunk j's products run
+      // (the fences around each refill would otherwise keep them apart)
+      [[maybe_unused]] bf16x8_t wk0, wk1;
+      if constexpr (QT == Dt::BF16 && KT == Dt::FP8) {
+        wk0 = fp8x8_to_bf16x8(dat[k][0][0], dat[k][0][1]);
+        wk1 = fp8x8_to_bf16x8(dat[k][0][2], dat[k][0][3]);
+      }
+#pragma unroll
+      for (int j = 0; j < L::kChunks; ++j) {
+        const u32x4_t kk = dat[k][j];
+        if (j < L::kVChunks) *reinterpret_cast<u32x4_t*>(vrow + (j * 4 + g) * 16) = kk;
+        if constexpr (KT == Dt::BF16) {
+          const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kk);
+#pragma unroll
+          for (int q = 0; q < QL; ++q) {
+            if (j & 1)
+              s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[q][j], s1[q], 0, 0, 0);
+            else
+              s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[q][j], s0[q], 0, 0, 0);
+          }
+        } else if constexpr (QT == Dt::BF16) {
+          const bf16x8_t k0 = wk0;
+          const bf16x8_t k1 = wk1;
+          if (j + 1 < L::kChunks) {
+            wk0 = fp8x8_to_bf16x8(dat[k][j + 1][0], dat[k][j + 1][1]);
+            wk1 = fp8x8_to_bf16x8(dat[k][j + 1][2], dat[k][j + 1][3]);
+          }
+#pragma unroll
+          for (int q = 0; q < QL; ++q) {
+            s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[q][2 * j], s0[q], 0, 0, 0);
+            s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[q][2 * j + 1], s1[q], 0, 0, 0);
+          }
+        } else {
+          const uint64_t k0 = (uint64_t)kk[0] | ((uint64_t)kk[1] << 32);
+          const uint64_t k1 = (uint64_t)kk[2] | ((uint64_t)kk[3] << 32);
+#pragma unroll
+          for (int q = 0; q < QL; ++q) {
+            s0[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k0, (long)q8[q][2 * j], s0[q], 0, 0, 0);
+            s1[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k1, (long)q8[q][2 * j + 1], s1[q], 0, 0, 0);
+          }
+        }
+        if constexpr (decltype(refill)::value) {
+          __builtin_amdgcn_sched_barrier(0);
+          dat[k][j] = *reinterpret_cast<const u32x4_t*>(nsrc + j * 64);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     // ---- previous tile's P.V (its weights and V were published before the last barrier)
@@ -944,15 +1226,42 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       }
     };
     make_p();
-    __syncthreads();
+    if constexpr (kLds) {
+      // Tile tt + 1 must be in LDS before the barrier that precedes its S^T.
+      // After its loads this wave has issued one page load, then (in this
+      // step) tile tt + 2's loads and one page load: kTileOps + 1, in the
+      // steady state and after the first tiles alike.  The last steps wait
+      // for everything.
+      if constexpr (decltype(refill)::value)
+        wait_vm<kTileOps + 1>();
+      else
+        wait_vm<0>();
+      lds_barrier();
+      // tile tt - 1's slot is free now (every wave finished its P.V before the
+      // barrier): tile tt + 3 goes there, during the next step's S^T
+      if constexpr (decltype(refill)::value) pend = next_rows;
+    } else {
+      __syncthreads();
+    }
     // ---- every wave sees the same four maxima, so the decision is workgroup-uniform
+    float mxw[QL][kWaves];
+#pragma unroll
+    for (int q = 0; q < QL; ++q)
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) mxw[q][ww] = sm.mx[buf][ww][q][c16];
+    if constexpr (kLds) {
+      // issued after the maxima (LDS reads complete in order, so the decision
+      // waits for the maxima only): tile tt + 1's K fragments, complete since
+      // the barrier, for the next S^T, and tile tt's V for the next P.V
+      read_k((k + 1) % kSlots);
+      load_v(tt);
+    }
     float mt[QL];
     bool need[QL];
     bool any = false;
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
-      mt[q] = fmaxf(fmaxf(sm.mx[buf][0][q][c16], sm.mx[buf][1][q][c16]),
-                    fmaxf(sm.mx[buf][2][q][c16], sm.mx[buf][3][q][c16]));
+      mt[q] = fmaxf(fmaxf(mxw[q][0], mxw[q][1]), fmaxf(mxw[q][2], mxw[q][3]));
       need[q] = mt[q] > m_run[q] + kRescaleSlack;
       any = any || need[q];
     }
@@ -967,8 +1276,12 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         m_run[q] = m_new;
       }
       make_p();  // nobody reads tile tt's weights before the next step
-      __syncthreads();
+      if constexpr (kLds)
+        lds_barrier();
+      else
+        __syncthreads();
     }
+    load_p(tt);  // the weights of tile tt, final now, for the next step's P.V
     // the row sums use the same bf16-rounded weights the P.V product sees
 #pragma unroll
     for (int q = 0; q < QL; ++q)
@@ -977,19 +1290,23 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         l_run[q] += __builtin_bit_cast(float, pw[q][i] << 16) + __builtin_bit_cast(float, pw[q][i] & 0xFFFF0000u);
   };
 
+  // LDS ring: every step of the main loop issues the loads its predecessor
+  // (or the start) left pending; of the last T mod D steps only the first does
+  using Y = std::true_type;
+  using N = std::false_type;
   int t0 = 0;
   for (; t0 + D <= T; t0 += D) {
-    step(std::integral_constant<int, 0>{}, t0, std::true_type{});
-    if constexpr (D > 1) step(std::integral_constant<int, 1>{}, t0 + 1, std::true_type{});
-    if constexpr (D > 2) step(std::integral_constant<int, 2>{}, t0 + 2, std::true_type{});
-    if constexpr (D > 3) step(std::integral_constant<int, 3>{}, t0 + 3, std::true_type{});
+    step(std::integral_constant<int, 0>{}, t0, Y{}, Y{});
+    if constexpr (D > 1) step(std::integral_constant<int, 1>{}, t0 + 1, Y{}, Y{});
+    if constexpr (D > 2) step(std::integral_constant<int, 2>{}, t0 + 2, Y{}, Y{});
+    if constexpr (D > 3) step(std::integral_constant<int, 3>{}, t0 + 3, Y{}, Y{});
   }
-  // the last T mod D tiles are already in the ring
-  if (t0 < T) step(std::integral_constant<int, 0>{}, t0, std::false_type{});
+  // the last T mod D tiles are already in the ring (LDS ring: or pending)
+  if (t0 < T) step(std::integral_constant<int, 0>{}, t0, N{}, Y{});
   if constexpr (D > 1)
-    if (t0 + 1 < T) step(std::integral_constant<int, 1>{}, t0 + 1, std::false_type{});
+    if (t0 + 1 < T) step(std::integral_constant<int, 1>{}, t0 + 1, N{}, N{});
   if constexpr (D > 2)
-    if (t0 + 2 < T) step(std::integral_constant<int, 2>{}, t0 + 2, std::false_type{});
+    if (t0 + 2 < T) step(std::integral_constant<int, 2>{}, t0 + 2, N{}, N{});
   static_assert(D <= 4, "ring depth above 4 needs more unrolled steps");
   if (T > 0) pv(T - 1);
 
@@ -999,6 +1316,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     const float l_tot = pair_sum32(pair_sum16(l_run[q]));
     if (g == 0) sm.lsum[w][q][c16] = l_tot;
   }
+  if constexpr (kLds) wait_vm<0>();  // no tile load may still land in the staging slot
   __syncthreads();
   // Lane (c16, g) holds, for block jb and i < 4, head c16 at column
   // 128w + (4g+i)*8 + jb: a contiguous run of 32 columns.  Written straight
@@ -1009,7 +1327,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // heads (float32) or 4 heads (bf16); reads follow the same wave's writes in
   // issue order.  Two-token passes have no registers to spare and store
   // directly.
-  uint8_t* const stage = &sm.v[0][0][0] + (size_t)w * kOutStageBytes;
+  uint8_t* const stage = sm.out_stage() + (size_t)w * kOutStageBytes;
 #pragma unroll
   for (int q = 0; q < QL; ++q) {
     if (q >= pc.ntok) break;  // uniform
@@ -1108,6 +1426,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   constexpr bool kCap = kForm == 2;
   static_assert(kGeneral || QL == 1, "several tokens per walk only in the general form");
   __shared__ Smem<KT, QL> sm;
+  constexpr int kScanPerThread = scan_per_thread<KT, QL>();
+  constexpr int kSeqTable = seq_table<KT, QL>();
   const int sh = kGeneral ? a.page_shift : 0;
   const bool paged = a.kv_last_page_len != nullptr && sh > 0;
   const bool multi = a.max_q_len > 1;  // several tokens per sequence: read qo_indptr[b + 1] too
@@ -1179,7 +1499,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   // below run; the piece issues the rows once its Q is on the way.  If the
   // split turns out to carry the cost, the pieces fetch their own.
   const int k = blockIdx.x;
-  Ring<KT, ring_depth<QT, KT, QL>()> ring;
+  RingOf<QT, KT, QL> ring;
   const Geo g0 = cost_free_geo(ip_first, ip_last, a.units, a.min_chunk, sh);
   {
     const int lo0 = k * g0.chunk;
