@@ -14,6 +14,11 @@ before the timed region.  The KV pool and its indices are replicated R times
 step cannot be served from the 256 MB last-level cache left warm by the
 previous step.
 
+Before the warm-up the bench runs about --settle-ms of untimed back-to-back
+steps: started after idle, the device runs the first ~25 ms of back-to-back
+steps up to ~1.35x slower, then holds a steady rate (--transient prints that
+start-up series as a diagnostic).  The timed steps measure the settled rate.
+
 Throughput is reported as algorithmic HBM bytes per second: KV rows read
 (576 B for fp8, 1152 B for bf16) + 4 B per page index + Q + bf16 output +
 both indptrs (+ the last-page lengths when pages hold several rows).  The
@@ -189,6 +194,10 @@ def main() -> int:
     ap.add_argument("--cpu-budget-single", type=float, default=4.0,
                     help="seconds of oracle work with one host thread (0: skip)")
     ap.add_argument("--rotate-bytes", type=float, default=2**30, help="KV bytes to rotate through (cache defeat)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed back-to-back steps for about this long before the warm-up (clock settling)")
+    ap.add_argument("--transient", action="store_true",
+                    help="after the bench line, time 20-step blocks right after an idle second (diagnostic)")
     ap.add_argument("--num-units", type=int, default=0)
     ap.add_argument("--min-chunk", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
@@ -276,6 +285,23 @@ def main() -> int:
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Settling: after idle the device first runs back-to-back steps up to ~1.35x slower, for ~25 ms, until
+    # its clocks settle at their sustained level.  The timed steps follow that many milliseconds of untimed
+    # back-to-back steps (the count from the time of a few probe steps), then the W warm-up steps.
+    settle_steps = 0
+    if args.settle_ms > 0:
+        for i in range(3):
+            step(i)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(5):
+            step(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        est_ms = max(t_start.elapsed_time(t_end) / 5, 1e-3)
+        settle_steps = int(math.ceil(args.settle_ms / est_ms))
+        for i in range(settle_steps):
+            step(i)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -460,12 +486,28 @@ def main() -> int:
                 "attention_time_over_probe": round(kern_avg_ms / same_avg_ms, 4),
             },
         },
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "wall_s_timed": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, opts, args.cpu_budget, args.cpu_budget_single)
     print(json.dumps(res), flush=True)
+    if args.transient:
+        # whole steps in blocks of 20 right after one idle second: the settling that the timed region skips
+        blk, nblk = 20, max(1, int(math.ceil(60.0 / (ms_per_step * 20))))
+        bev = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
+        torch.cuda.synchronize()
+        time.sleep(1.0)
+        bev[0].record(stream)
+        for b in range(nblk):
+            for i in range(blk):
+                step(b * blk + i)
+            bev[b + 1].record(stream)
+        torch.cuda.synchronize()
+        series = [round(bev[b].elapsed_time(bev[b + 1]) / blk * 1e3, 2) for b in range(nblk)]
+        print(json.dumps({"transient_us_per_step_20_step_blocks_after_idle": series,
+                          "settled_us_per_step": round(ms_per_step * 1e3, 2)}), flush=True)
     return 0
 
 
