@@ -366,7 +366,7 @@ def main() -> int:
             cast_us[label] = round(t_start.elapsed_time(t_end) / n_diag * 1e3, 2)
         del q8, qs_tmp
     probe = torch.ones(1 << 30, dtype=torch.uint8, device=dev)  # 1 GiB
-    sink = torch.empty(binding.MLA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    sink = torch.empty(binding.read_probe_sink_words(1 << 30), dtype=torch.int32, device=dev)
     for _ in range(3):
         binding.mla_read_probe(probe, sink, stream)
     torch.cuda.synchronize()
@@ -385,6 +385,7 @@ def main() -> int:
     n_slice = (alg_bytes + 15) // 16 * 16
     n_rot = max(2, math.ceil(args.rotate_bytes / n_slice))
     slab = torch.ones(n_slice * n_rot, dtype=torch.uint8, device=dev)
+    sink = torch.empty(binding.read_probe_sink_words(n_slice), dtype=torch.int32, device=dev)
     slices = [slab[i * n_slice:(i + 1) * n_slice] for i in range(n_rot)]
     for i in range(2 * n_rot):
         binding.mla_read_probe(slices[i % n_rot], sink, stream)
@@ -472,7 +473,8 @@ def main() -> int:
             "plan_us_per_call_host": round(plan_us, 1),
             "q_cast_us": cast_us,
             "read_probe": {
-                "kind": "mla_read_probe: 16-byte streaming reads of 1 GiB, 1024 workgroups x 256 threads, same device",
+                "kind": "mla_read_probe: one pass of 512-thread workgroups, four 16-byte non-temporal loads per "
+                        "thread, over 1 GiB, same device",
                 "GBps": round(probe_gbs, 1),
                 "attention_frac_of_probe": round(achieved / probe_gbs, 4),
             },

@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 3
+#define MLA_DECODE_ABI_VERSION 4
 
 typedef enum {
   MLA_OK = 0,
@@ -314,15 +314,18 @@ mla_status mla_decode_reduce(const float* part_o, const float* part_lse, const i
 
 /*
  * Diagnostic, not part of the decode path: read `bytes` of device memory at
- * `buf` once, with 16-byte loads from 1024 workgroups of 256 threads, and
- * store one 32-bit word per workgroup to `sink` (the xor of the words it
- * read).  Timed around its launch, this gives the device's practical
- * streaming read rate, beside which the decode kernels' bandwidth can be set.
+ * `buf` once, in one pass of workgroups of 512 threads that each read their
+ * own MLA_READ_PROBE_BYTES_PER_WORD contiguous bytes (four 16-byte
+ * non-temporal loads per thread, all in flight together), and store one
+ * 32-bit word per workgroup to `sink`: word k is the xor of the 32-bit words
+ * in bytes [k * MLA_READ_PROBE_BYTES_PER_WORD, (k + 1) * ...) of `buf`.
+ * Timed around its launch, this gives the device's plain streaming read rate
+ * for that many bytes, beside which the decode kernels' bandwidth can be set.
  * `buf` must be 16-byte aligned and `bytes` a positive multiple of 16; `sink`
- * must hold at least MLA_READ_PROBE_SINK_WORDS words.  Otherwise
- * MLA_ERR_INVALID_ARG, before any launch.
+ * must hold at least ceil(bytes / MLA_READ_PROBE_BYTES_PER_WORD) words.
+ * Otherwise MLA_ERR_INVALID_ARG, before any launch.
  */
-#define MLA_READ_PROBE_SINK_WORDS 1024
+#define MLA_READ_PROBE_BYTES_PER_WORD 32768
 mla_status mla_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream);
 
 /* Static description of a status code.  Derived: the pages define no error

@@ -32,7 +32,8 @@ __all__ = [
     "mla_status_string",
     "mla_decode_abi_version",
     "mla_read_probe",
-    "MLA_READ_PROBE_SINK_WORDS",
+    "MLA_READ_PROBE_BYTES_PER_WORD",
+    "read_probe_sink_words",
     "mla_decode_workspace_size",
     "mla_decode_plan",
     "mla_decode_run",
@@ -184,14 +185,20 @@ def mla_decode_abi_version() -> int:
     return int(lib().mla_decode_abi_version())
 
 
-MLA_READ_PROBE_SINK_WORDS = 1024
+MLA_READ_PROBE_BYTES_PER_WORD = 32768
+
+
+def read_probe_sink_words(nbytes: int) -> int:
+    """Sink words mla_read_probe needs for a buffer of nbytes: one per probe workgroup."""
+    return -(-nbytes // MLA_READ_PROBE_BYTES_PER_WORD)
 
 
 def mla_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     """Diagnostic streaming read of all of `buf` (see the header); `sink` holds one int32 per probe workgroup."""
-    if sink.dtype != torch.int32 or sink.numel() < MLA_READ_PROBE_SINK_WORDS:
-        raise ValueError(f"sink must be int32 with at least {MLA_READ_PROBE_SINK_WORDS} elements")
-    code = lib().mla_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(), _stream(stream))
+    nbytes = buf.numel() * buf.element_size()
+    if sink.dtype != torch.int32 or sink.numel() < read_probe_sink_words(nbytes):
+        raise ValueError(f"sink must be int32 with at least {read_probe_sink_words(nbytes)} elements")
+    code = lib().mla_read_probe(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(stream))
     _check(code, "mla_read_probe")
 
 

@@ -225,11 +225,13 @@ const char* mla_status_string(mla_status status) {
 int32_t mla_decode_abi_version(void) { return MLA_DECODE_ABI_VERSION; }
 
 mla_status mla_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream) {
-  static_assert(mla::kProbeBlocks == MLA_READ_PROBE_SINK_WORDS, "one sink word per probe workgroup");
+  static_assert(mla::kProbeWords * 16 == MLA_READ_PROBE_BYTES_PER_WORD, "one sink word per probe workgroup");
   if (buf == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 ||
-      (reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || sink_words < (size_t)MLA_READ_PROBE_SINK_WORDS)
+      (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
     return MLA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(mla::mla_read_probe_kernel, dim3(mla::kProbeBlocks), dim3(256), 0, stream,
+  const size_t groups = (bytes + MLA_READ_PROBE_BYTES_PER_WORD - 1) / MLA_READ_PROBE_BYTES_PER_WORD;
+  if (sink_words < groups || groups > 0x7fffffffu) return MLA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(mla::mla_read_probe_kernel, dim3((unsigned)groups), dim3(mla::kProbeThreads), 0, stream,
                      static_cast<const mla::u32x4_t*>(buf), (int64_t)(bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

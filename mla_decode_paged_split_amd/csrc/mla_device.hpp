@@ -1697,32 +1697,41 @@ __global__ __launch_bounds__(64) void mla_reduce_external_kernel(const float* pa
                   out + ((size_t)b * kHeads + h) * kVDim, lse_out != nullptr ? lse_out + (size_t)b * kHeads + h : nullptr);
 }
 
-// Streaming read probe (a diagnostic): workgroup k reads its own contiguous
-// share [k * per, (k + 1) * per) of the 16-byte words, four loads in flight per
-// thread (a grid-wide stride would put every workgroup in one narrow moving
-// window of addresses, which camps on memory channels); the words past the
-// last whole share go to the first threads of the grid.  Each workgroup stores
-// the xor of what it read so that no load can be dropped.
-constexpr int kProbeBlocks = 1024;
-__global__ __launch_bounds__(256) void mla_read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16,
-                                                             uint32_t* __restrict__ sink) {
-  __shared__ uint32_t red;
-  const int64_t per = n16 / gridDim.x;
-  const u32x4_t* share = p + (int64_t)blockIdx.x * per;
-  int64_t i = threadIdx.x;
-  u32x4_t acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * 256 < per; i += 4 * 256) {
-    const u32x4_t a = share[i], b = share[i + 256], c = share[i + 512], d = share[i + 768];
-    acc ^= a ^ b ^ c ^ d;
+// Streaming read probe (a diagnostic): one pass, no loop.  Workgroup k of 512
+// threads reads the 2048 sixteen-byte words [2048 k, 2048 k + 2048), four
+// loads per thread, all issued before any is used, with the non-temporal hint
+// (of the plain read forms measured on this device, one-shot workgroups of
+// 512 threads x 4 non-temporal loads read a few hundred MB fastest).  Loads
+// past the end read the last word and are then dropped, so every load is
+// unconditional.  Each workgroup stores the xor of what it read so that no
+// load can be dropped.
+constexpr int kProbeThreads = 512;
+constexpr int kProbeLoads = 4;
+constexpr int kProbeWords = kProbeThreads * kProbeLoads;
+__global__ __launch_bounds__(kProbeThreads) void mla_read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16,
+                                                                       uint32_t* __restrict__ sink) {
+  __shared__ uint32_t red[kProbeThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kProbeWords + threadIdx.x;
+  u32x4_t v[kProbeLoads];
+#pragma unroll
+  for (int u = 0; u < kProbeLoads; ++u) {
+    const int64_t i = base + (int64_t)u * kProbeThreads;
+    v[u] = __builtin_nontemporal_load(p + (i < n16 ? i : n16 - 1));
   }
-  for (; i < per; i += 256) acc ^= share[i];
-  const int64_t tail = (int64_t)gridDim.x * per + (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (tail < n16) acc ^= p[tail];
-  if (threadIdx.x == 0) red = 0u;
+  uint32_t x = 0u;
+#pragma unroll
+  for (int u = 0; u < kProbeLoads; ++u)
+    if (base + (int64_t)u * kProbeThreads < n16) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
-  atomicXor(&red, acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
-  __syncthreads();
-  if (threadIdx.x == 0) sink[blockIdx.x] = red;
+  if (threadIdx.x == 0) {
+    uint32_t r = 0u;
+#pragma unroll
+    for (int i = 0; i < kProbeThreads / 64; ++i) r ^= red[i];
+    sink[blockIdx.x] = r;
+  }
 }
 
 __global__ void mla_fill_i32_kernel(int32_t* p, int n, int32_t v) {

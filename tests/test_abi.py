@@ -42,7 +42,7 @@ def test_struct_layout_matches_header():
 
 
 def test_abi_version_and_status_strings():
-    assert B.mla_decode_abi_version() == 3
+    assert B.mla_decode_abi_version() == 4
     for code in range(5):
         s = B.mla_status_string(code)
         assert s.startswith("MLA_")
