@@ -578,17 +578,19 @@ __device__ __forceinline__ void zero_row_by_thread(uint16_t* out_row) {
 // Row `pr` of a piece that starts at index position ip0 and has nrows rows
 // lives in page kv_indices[ip0 + pr / page_size], slot pr % page_size
 // (page_size = 2^sh), i.e. pool row page * page_size + slot.  Rows at or past
-// nrows stand for the piece's first row instead, which is always valid.
+// nrows stand for the piece's last row instead: always valid, and the ring's
+// loads past the end (issued in the last steps, never used) then read what
+// the last tile has just brought into the cache instead of waiting on memory.
 // The page load and the row composition are separate so that the ring can
 // keep the raw page index in flight and compose the row only when it issues
 // the tile's loads (using a loaded value at once would wait for it).
 __device__ __forceinline__ int piece_page(const int32_t* __restrict__ kv_indices, int ip0, int nrows, int pr,
                                           int sh) {
-  return kv_indices[ip0 + ((pr < nrows ? pr : 0) >> sh)];
+  return kv_indices[ip0 + ((pr < nrows ? pr : nrows - 1) >> sh)];
 }
 
 __device__ __forceinline__ int page_row(int page, int nrows, int pr, int sh) {
-  return (page << sh) | ((pr < nrows ? pr : 0) & ((1 << sh) - 1));
+  return (page << sh) | ((pr < nrows ? pr : nrows - 1) & ((1 << sh) - 1));
 }
 
 // The register ring of one piece: the rows of D tiles in flight (tile t in
@@ -728,7 +730,7 @@ __device__ __forceinline__ void issue_ring_indices(const int32_t* __restrict__ k
 
 // Start the loads of the ring's first D tiles (in the steady state's slot
 // order, kept by scheduling barriers so the loop's wait counts stay exact).
-// Rows at or past nrows load the first page's slot 0 (never used).
+// Rows at or past nrows load the piece's last row (never used).
 template <Dt KT, class R>
 __device__ __forceinline__ void issue_ring_rows(const void* kv, int nrows, int sh, R& r) {
   using L = KvLayout<KT>;
@@ -1131,7 +1133,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       auto& idxn = ring.next;
       uint8_t* vrow = &sm.v[buf][16 * w + c16][0];
       // The slot is refilled with tile tt + D chunk by chunk, each load issued
-      // right after its chunk is used (rows past the piece clamp to its first
+      // right after its chunk is used (rows past the piece clamp to its last
       // row, so every steady-state trip issues the same loads and the compiler's
       // wait counts stay exact).  Spread over the products, the four waves' loads
       // reach the address unit a few at a time instead of as one burst.
@@ -1230,9 +1232,9 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       // Tile tt + 1 must be in LDS before the barrier that precedes its S^T.
       // After its loads this wave has issued one page load, then (in this
       // step) tile tt + 2's loads and one page load: kTileOps + 1, in the
-      // steady state and after the first tiles alike.  The last steps wait
-      // for everything.
-      if constexpr (decltype(refill)::value)
+      // steady state and after the first tiles alike.  A step that issues no
+      // tile waits for everything.
+      if constexpr (decltype(pend_in)::value)
         wait_vm<kTileOps + 1>();
       else
         wait_vm<0>();
@@ -1290,24 +1292,53 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         l_run[q] += __builtin_bit_cast(float, pw[q][i] << 16) + __builtin_bit_cast(float, pw[q][i] & 0xFFFF0000u);
   };
 
-  // LDS ring: every step of the main loop issues the loads its predecessor
-  // (or the start) left pending; of the last T mod D steps only the first does
   using Y = std::true_type;
   using N = std::false_type;
-  int t0 = 0;
-  for (; t0 + D <= T; t0 += D) {
-    step(std::integral_constant<int, 0>{}, t0, Y{}, Y{});
-    if constexpr (D > 1) step(std::integral_constant<int, 1>{}, t0 + 1, Y{}, Y{});
-    if constexpr (D > 2) step(std::integral_constant<int, 2>{}, t0 + 2, Y{}, Y{});
-    if constexpr (D > 3) step(std::integral_constant<int, 3>{}, t0 + 3, Y{}, Y{});
-  }
-  // the last T mod D tiles are already in the ring (LDS ring: or pending)
-  if (t0 < T) step(std::integral_constant<int, 0>{}, t0, N{}, Y{});
-  if constexpr (D > 1)
-    if (t0 + 1 < T) step(std::integral_constant<int, 1>{}, t0 + 1, N{}, N{});
-  if constexpr (D > 2)
-    if (t0 + 2 < T) step(std::integral_constant<int, 2>{}, t0 + 2, N{}, N{});
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
   static_assert(D <= 4, "ring depth above 4 needs more unrolled steps");
+  if constexpr (kLds) {
+    // Whole turns while tiles remain past the turn, then the last 1..4 tiles,
+    // whose steps issue only tiles of the piece (when T is a multiple of 4,
+    // the usual case, no load past the piece goes out and no step waits for
+    // one): 4 left: the first two steps issue the last two tiles; 3 left:
+    // the first issues the last; 2 or 1 left: they are in flight already.
+    int t0 = 0;
+    for (; t0 + 4 < T; t0 += 4) {
+      step(S0{}, t0, Y{}, Y{});
+      step(S1{}, t0 + 1, Y{}, Y{});
+      step(S2{}, t0 + 2, Y{}, Y{});
+      step(S3{}, t0 + 3, Y{}, Y{});
+    }
+    const int r = T - t0;
+    if (r == 4) {
+      step(S0{}, t0, Y{}, Y{});
+      step(S1{}, t0 + 1, N{}, Y{});
+    } else if (r == 3) {
+      step(S0{}, t0, N{}, Y{});
+    } else if (r > 0) {
+      step(S0{}, t0, N{}, N{});
+    }
+    if (r == 2 || r == 3) step(S1{}, t0 + 1, N{}, N{});
+    if (r >= 3) step(S2{}, t0 + 2, N{}, N{});
+    if (r == 4) step(S3{}, t0 + 3, N{}, N{});
+  } else {
+    int t0 = 0;
+    for (; t0 + D <= T; t0 += D) {
+      step(S0{}, t0, Y{}, N{});
+      if constexpr (D > 1) step(S1{}, t0 + 1, Y{}, N{});
+      if constexpr (D > 2) step(S2{}, t0 + 2, Y{}, N{});
+      if constexpr (D > 3) step(S3{}, t0 + 3, Y{}, N{});
+    }
+    // the last T mod D tiles are already in the ring
+    if (t0 < T) step(S0{}, t0, N{}, N{});
+    if constexpr (D > 1)
+      if (t0 + 1 < T) step(S1{}, t0 + 1, N{}, N{});
+    if constexpr (D > 2)
+      if (t0 + 2 < T) step(S2{}, t0 + 2, N{}, N{});
+  }
   if (T > 0) pv(T - 1);
 
   // ---- finish: per-head row sums of the 4 waves, then this wave's 128 columns
