@@ -12,7 +12,7 @@ Two kinds of summary:
 
 Usage:
   python -m mla_decode_paged_split_amd.profile_summary trace <stats.csv> <out.md> "<command>" \
-      [<trace.csv> <warm-up steps> <timed steps> <bench log>]
+      [<trace.csv> <bench log>]
   python -m mla_decode_paged_split_amd.profile_summary pmc <workload> <fetch.csv> <write.csv> \
       <copy_fetch.csv> <copy_write.csv> <algorithmic_bytes> <out.json> "<commands>"
   python -m mla_decode_paged_split_amd.profile_summary mfma <counters.csv> <out.md> "<command>" <flops> <peak>
@@ -41,11 +41,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | None = None, warmup: int = 0,
-                  steps: int = 0, bench_log: str | None = None) -> None:
-    """The --stats table, plus (with the per-dispatch trace) the attention launches of the bench's second
-    timed region, which are the launches its HIP events time (the bench issues warm-up, then the steps of
-    region 1, then those of region 2, then its diagnostics), and the bench's own line from that run."""
+def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | None = None,
+                  bench_log: str | None = None) -> None:
+    """The --stats table, plus (with the per-dispatch trace and the bench's log) the attention launches of
+    the bench's two timed regions, with the KV copies rotated: region 1 (whole steps back to back) and
+    region 2 (attention launches back to back, the roofline's source).  The bench issues its settling
+    steps, the warm-up, region 1, region 2, then diagnostics (per-launch events, one KV copy reused, ...),
+    which the per-kernel table averages in but the region figures leave out."""
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [
         "# Kernel trace summary",
@@ -54,7 +56,8 @@ def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | No
         "",
         f"Kernel sources hash: `{kernel_source_hash()}`",
         "",
-        "All dispatches (warm-up and both timed regions):",
+        "All dispatches (settling, warm-up, both timed regions and the diagnostics, some with one KV copy "
+        "reused and so partly cache-warm):",
         "",
         "| kernel | calls | avg us | min us | max us | share |",
         "|---|---|---|---|---|---|",
@@ -64,27 +67,34 @@ def trace_summary(stats_csv: str, out_md: str, command: str, trace_csv: str | No
             f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
             f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |"
         )
-    if trace_csv and steps > 0:
-        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(open(trace_csv))
-             if ATTENTION in r["Kernel_Name"]]
-        last = d[warmup + steps:warmup + 2 * steps]
-        lines += [
-            "",
-            f"Attention launches of the event-timed region (launches {warmup + steps + 1}-{warmup + 2 * steps} "
-            f"of {len(d)}): mean {statistics.mean(last):.2f} us, median {statistics.median(last):.2f} us, "
-            f"min {min(last):.2f} us, max {max(last):.2f} us.",
-        ]
+    bench = None
     if bench_log:
         for line in open(bench_log):
             if line.startswith("{") and '"roofline"' in line:
-                b = json.loads(line)
-                r = b["roofline"]
+                bench = json.loads(line)
+    if trace_csv and bench:
+        st = bench.get("settle", {})
+        pre = int(st.get("timing_probe_steps", 0)) + int(st.get("steps", 0)) + int(bench["warmup"])
+        k = int(bench["steps"])
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(open(trace_csv))
+             if ATTENTION in r["Kernel_Name"]]
+        for label, lo in (("region 1 (whole steps back to back)", pre),
+                          ("region 2 (attention launches back to back; the roofline's source)", pre + k)):
+            seg = d[lo:lo + k]
+            if len(seg) == k:
                 lines += [
                     "",
-                    f"The bench line of the same profiled run: step {b['us_per_call']} us, attention launch by HIP "
-                    f"events mean {r['kernel_avg_us']} us / median {r['kernel_median_us']} us (the events also "
-                    f"enclose the profiler's dispatch handling), roofline frac {r['frac']}.",
+                    f"Attention launches of {label}, launches {lo + 1}-{lo + k} of {len(d)}: mean "
+                    f"{statistics.mean(seg):.2f} us, median {statistics.median(seg):.2f} us, "
+                    f"min {min(seg):.2f} us, max {max(seg):.2f} us.",
                 ]
+    if bench:
+        r = bench["roofline"]
+        lines += [
+            "",
+            f"The bench line of the same profiled run: step {bench['us_per_call']} us; attention launch "
+            f"{r['kernel_avg_us']} us ({r.get('kernel_timing', 'HIP events')}), roofline frac {r['frac']}.",
+        ]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -172,9 +182,7 @@ def mfma_summary(counter_csv: str, out_md: str, command: str, flops_per_launch: 
 if __name__ == "__main__":
     kind = sys.argv[1]
     if kind == "trace":
-        trace_summary(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:6] or [None]),
-                      int(sys.argv[6]) if len(sys.argv) > 6 else 0, int(sys.argv[7]) if len(sys.argv) > 7 else 0,
-                      *(sys.argv[8:9] or [None]))
+        trace_summary(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:7] + [None, None])[:2])
     elif kind == "mfma":
         mfma_summary(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), float(sys.argv[6]))
     elif kind == "pmc":
