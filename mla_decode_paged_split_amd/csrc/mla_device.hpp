@@ -794,7 +794,7 @@ struct Logit {
 // (pages of one row, no soft-cap), with both compiled out of the loop.
 template <Dt QT, Dt KT, int QL, bool kGeneral, bool kCap, class RingT>
 __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& pc, const Logit logit,
-                             float out_mul, RingT& ring) {
+                             float out_mul, RingT& ring, const DmaLanes& dl) {
   using L = KvLayout<KT>;
   constexpr int D = RingT::D;
   constexpr bool kLds = lds_ring<KT, QL>();
@@ -804,11 +804,9 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   const int g = lane >> 4;
   const int sh = kGeneral ? a.page_shift : 0;
   const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
-  // LDS ring: the per-lane constants of the tile loads, the rows of the tile
-  // whose loads the next step issues, this wave's 16 rows in a slot (the wave
-  // index made a scalar once) and the next S^T's K fragments
-  [[maybe_unused]] DmaLanes dl;
-  if constexpr (kLds) dl = dma_lanes();
+  // LDS ring: the rows of the tile whose loads the next step issues (dl: the
+  // per-lane constants of the tile loads), this wave's 16 rows in a slot (the
+  // wave index made a scalar once) and the next S^T's K fragments
   [[maybe_unused]] DmaRows pend;
   [[maybe_unused]] const int wrow_bytes = 16 * __builtin_amdgcn_readfirstlane(w) * kF8Row;
   [[maybe_unused]] u32x4_t kcur[KvLayout<KT>::kChunks];
@@ -921,14 +919,27 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // the ring is primed: tiles 0..D-1 in flight (fp8 KV: 0..2 in flight, tile 0
   // in LDS), pages of the next ones loaded
   auto page_index = [&](int tt) { return piece_page(a.kv_indices, pc.ip0, pc.nrows, tt * kTileRows + my_row, sh); };
-  // fp8 KV: the K fragments of the tile in slot `sl`: lane (c16, g) reads chunks 4j + g of row
-  // 16w + c16 (kpos(16w + c16, .) == kpos(c16, .))
+  // LDS ring: the K fragments of the tile in slot `sl`: lane (c16, g) reads
+  // chunks 4j + g of row 16w + c16, at kpos(c16, 4j + g).  With a = (c16 >> 2) & 3
+  // that position is 4 (j ^ 2 (a & 1)) + (g ^ a) for j < 8 and 32 + (g ^ a)
+  // for j = 8, so each chunk's byte offset is one of three per-lane bases plus
+  // 64 j: a constant the LDS reads take as an immediate offset.
+  [[maybe_unused]] uint32_t k_lo = 0, k_hi = 0, k_v8 = 0;
+  if constexpr (kLds) {
+    const int ka = (c16 >> 2) & 3;
+    const uint32_t kb = (uint32_t)(my_row * kF8Row + 16 * (g ^ ka));
+    k_lo = kb + 128u * (ka & 1);  // chunks j with (j & 2) == 0
+    k_hi = kb - 128u * (ka & 1);  // chunks j with (j & 2) != 0
+    k_v8 = kb + 512u;             // chunk 8 (rope part)
+  }
   auto read_k = [&](int sl) {
     if constexpr (kLds) {
-      const uint8_t* krow = &sm.k[sl][0][0] + my_row * kF8Row;
+      const uint8_t* kslot = &sm.k[sl][0][0];
 #pragma unroll
-      for (int j = 0; j < L::kChunks; ++j)
-        kcur[j] = *reinterpret_cast<const u32x4_t*>(krow + (kpos(c16, 4 * j + g) << 4));
+      for (int j = 0; j < L::kChunks; ++j) {
+        const uint32_t off = j == 8 ? k_v8 : ((j & 2) ? k_hi : k_lo) + 64u * (j == 8 ? 0 : j);
+        kcur[j] = *reinterpret_cast<const u32x4_t*>(kslot + off);
+      }
     }
   };
   read_k(0);  // LDS ring: tile 0 is complete since the start's barrier
@@ -1490,6 +1501,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   const int32_t ip_last = a.kv_indptr[a.batch];
   // these loads go out before the ring's, so using them never waits for the ring's indices
   __builtin_amdgcn_sched_barrier(0);
+  // LDS ring: the per-lane constants of the tile loads, computed while the
+  // first round trip is in flight (an empty asm use keeps the compiler from
+  // sinking their ~100 instructions to the first piece, after the barriers,
+  // where they would delay its first tile)
+  [[maybe_unused]] DmaLanes dl;
+  if constexpr (lds_ring<KT, QL>()) {
+    dl = dma_lanes();
+#pragma unroll
+    for (int i = 0; i < 9; ++i) asm volatile("" ::"v"(dl.src[i]), "v"(dl.off[i]));
+  }
 
   // The first round trip's values go to the LDS sequence table before the
   // ring's indices are requested, so no register waiting on them stays live
@@ -1624,7 +1645,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       pc.slot = complete ? -1 : slot * a.max_q_len + tau0;
       pc.complete = complete;
       if (!primed || b != bmin || tau0 != 0) issue_ring_indices(a.kv_indices, pc.ip0, nrows, sh, ring);
-      attend_piece<QT, KT, QL, kGeneral, kCap>(a, sm, pc, logit, out_mul, ring);
+      attend_piece<QT, KT, QL, kGeneral, kCap>(a, sm, pc, logit, out_mul, ring, dl);
     }
     if (!complete && a.fused && q_len > 0) {
       __threadfence();
