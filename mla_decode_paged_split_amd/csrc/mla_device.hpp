@@ -965,9 +965,10 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // k-step ks covers rows 32ks..32ks+31; slot s of lane group g is row
   // R = 32ks + (s/4)*16 + g*4 + s%4, which is wave 2ks + s/4's row g*4 + s%4.
   // Block jb holds columns 128w + m*8 + jb, m = 0..15; lane c16 feeds m = c16.
-  // LDS ring: the next P.V's operands, read from LDS right after the barrier
-  // that publishes them (V of the tile, still in its slot; its weights), so
-  // that the next step's products wait for no LDS read
+  // LDS ring: the next P.V's operands, read from LDS ahead of it (V of the
+  // tile, still in its slot, right after the previous P.V; its weights right
+  // after the barrier that publishes them), so that the next step's products
+  // wait for no LDS read
   [[maybe_unused]] u32x2_t vreg[2][8];
   [[maybe_unused]] u32x2_t preg[QL][2][2];
   // V of tile tt: columns 128w + 8 c16 .. + 7 of row R lie in chunk 8w + c16 / 2,
@@ -1139,6 +1140,17 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       }
       // the page of the tile this slot receives after tile tt + 2
       if constexpr (decltype(pend_in)::value) ring.first[(k + 2) % kSlots] = page_index(tt + 2 * kSlots - 2);
+      // Tile tt + 1's rows of this wave are its own loads, so its K fragments
+      // need no barrier, only those loads: after them this wave has issued
+      // one page load, then (in this step) tile tt + 2's loads and one page
+      // load, kTileOps + 1 in every step that issues a tile (one that issues
+      // none waits for everything).  Read now, they arrive while the P.V and
+      // the softmax run instead of after the barrier.
+      if constexpr (decltype(pend_in)::value)
+        wait_vm<kTileOps + 1>();
+      else
+        wait_vm<0>();
+      read_k((k + 1) % kSlots);
     } else {
       auto& dat = ring.dat;
       auto& idxn = ring.next;
@@ -1205,6 +1217,9 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     }
     // ---- previous tile's P.V (its weights and V were published before the last barrier)
     if (tt > 0) pv(tt - 1);
+    // LDS ring: tile tt's V for the next P.V (the tile is whole since the last
+    // barrier; its slot is rewritten only after the next one)
+    if constexpr (kLds) load_v(tt);
     // ---- scores (log2 domain), masked past the rows each token sees
     float x[QL][4];
     float mx[QL];
@@ -1240,15 +1255,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     };
     make_p();
     if constexpr (kLds) {
-      // Tile tt + 1 must be in LDS before the barrier that precedes its S^T.
-      // After its loads this wave has issued one page load, then (in this
-      // step) tile tt + 2's loads and one page load: kTileOps + 1, in the
-      // steady state and after the first tiles alike.  A step that issues no
-      // tile waits for everything.
-      if constexpr (decltype(pend_in)::value)
-        wait_vm<kTileOps + 1>();
-      else
-        wait_vm<0>();
+      // every wave's rows of tile tt + 1 are in LDS (each waited for its own)
       lds_barrier();
       // tile tt - 1's slot is free now (every wave finished its P.V before the
       // barrier): tile tt + 3 goes there, during the next step's S^T
@@ -1262,13 +1269,6 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     for (int q = 0; q < QL; ++q)
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) mxw[q][ww] = sm.mx[buf][ww][q][c16];
-    if constexpr (kLds) {
-      // issued after the maxima (LDS reads complete in order, so the decision
-      // waits for the maxima only): tile tt + 1's K fragments, complete since
-      // the barrier, for the next S^T, and tile tt's V for the next P.V
-      read_k((k + 1) % kSlots);
-      load_v(tt);
-    }
     float mt[QL];
     bool need[QL];
     bool any = false;
