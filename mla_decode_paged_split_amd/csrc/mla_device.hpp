@@ -413,14 +413,14 @@ __device__ __forceinline__ uint64_t bf16x8_to_e4m3fn(u32x4_t w) {
 // sequence b then occupies [kv_indptr[b] - base + cost * b, ... + its
 // positions) of a "cost space" whose gaps belong to no one, and the shares
 // cut that space.  Each piece a workgroup walks has a fixed price (a ring
-// start, the Q load, the finish) of about three tiles, so without the term a
+// start, the Q load, the finish) of three to four tiles, so without the term a
 // share that holds many sequence starts (many short sequences, or ragged
 // lengths) takes that price many times while its neighbours take it once.
 // The cost is left out (0) only where it cannot help: every sequence has the
 // same length, at least kCostFreeMinRows rows, and that length and the share
 // size divide one into the other, so every share holds whole sequences or
 // whole fractions of one.
-constexpr int kPieceCostRows = 192;
+constexpr int kPieceCostRows = 256;
 constexpr int kCostFreeMinRows = 1024;
 
 struct Geo {

@@ -20,6 +20,7 @@ from mla_cases import DevCase, Timer, assert_parity, log, oracle_ref, to64
 pytestmark = pytest.mark.gpu
 
 PAIRS = [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8")]
+PIECE_COST_ROWS = 256  # the split's per-sequence cost, in rows
 LENGTHS = [1, 2, 31, 32, 33, 64, 100, 257, 513, 1000, 2053]
 # (num_units, min_chunk, flags): one share for everything, a few shares, many
 # shares, and 32-row shares (up to 65 pieces for the 2053-row sequence)
@@ -483,7 +484,7 @@ def test_batch_beyond_lds_table(gpu, qd, kd):
     # equal lengths of 1024 rows and shares of 2048 (515 units): without the cost; then the same with one
     # length changed past the LDS table, which only the scan from memory sees: with it
     seqs = [0, 1, 513, 1023, 1024, 1025, 1027, 1029]
-    for lens, cost in (([1024] * 1030, 0), ([1024] * 1027 + [1023] + [1024] * 2, 192)):
+    for lens, cost in (([1024] * 1030, 0), ([1024] * 1027 + [1023] + [1024] * 2, PIECE_COST_ROWS)):
         spec = synth.CaseSpec(batch=1030, q_dtype=qd, kv_dtype=kd, lengths=lens, permuted=True, seed=3301)
         case = synth.make_case(spec)
         dc = DevCase(case, gpu)
@@ -505,7 +506,7 @@ def split_record(dec: binding.Decoder) -> list:
 
 
 def expected_split(case, units: int, min_chunk: int) -> list:
-    """The split rule restated on the host: positions are pages; every sequence costs 192 rows of
+    """The split rule restated on the host: positions are pages; every sequence costs PIECE_COST_ROWS of
     positions unless all have one length of at least 1024 rows that the share size divides or is
     divided by."""
     sh = case.spec.page_size.bit_length() - 1
@@ -523,7 +524,7 @@ def expected_split(case, units: int, min_chunk: int) -> list:
     if all(x == L for x in lens) and L >= max(1, 1024 >> sh) and (L % c0 == 0 or c0 % L == 0):
         cost, total, chunk = 0, pos, c0
     else:
-        cost = max(1, 192 >> sh)
+        cost = max(1, PIECE_COST_ROWS >> sh)
         total = pos + cost * len(lens)
         chunk = share(total)
     return [ind[0], cost, total, chunk, max(1, -(-total // chunk))]
@@ -531,10 +532,10 @@ def expected_split(case, units: int, min_chunk: int) -> list:
 
 @pytest.mark.parametrize("lens,page,units,cost", [
     ([4096] * 8, 1, 256, 0),  # equal, long, shares of 128 divide the length
-    ([5000] * 3, 1, 256, 192),  # equal and long, but shares of 64 neither divide nor are divided by 5000
-    ([512] * 16, 1, 256, 192),  # equal but short
-    ([8192, 8191, 8192, 8192], 1, 64, 192),  # one length differs
-    ([8010] * 4, 16, 256, 12),  # pages of 16: 501 positions each, shares of 16 positions; cost 192 >> 4
+    ([5000] * 3, 1, 256, PIECE_COST_ROWS),  # equal and long, but shares of 64 neither divide nor are divided by 5000
+    ([512] * 16, 1, 256, PIECE_COST_ROWS),  # equal but short
+    ([8192, 8191, 8192, 8192], 1, 64, PIECE_COST_ROWS),  # one length differs
+    ([8010] * 4, 16, 256, PIECE_COST_ROWS >> 4),  # pages of 16: 501 positions each, shares of 16 positions
     ([8192] * 64, 16, 256, 0),  # pages of 16, shares of 128 positions
 ])
 def test_split_rule(gpu, lens, page, units, cost):
