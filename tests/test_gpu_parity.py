@@ -498,6 +498,37 @@ def test_batch_beyond_lds_table(gpu, qd, kd):
         del dc, case
 
 
+@pytest.mark.parametrize("qd,kd,batch", [
+    ("bf16", "fp8", 512), ("bf16", "fp8", 513), ("fp8", "fp8", 512), ("fp8", "fp8", 513),  # LDS ring: 512
+    ("bf16", "bf16", 1024), ("bf16", "bf16", 1025),  # register ring: a table of 1024 sequences
+])
+def test_batch_at_lds_table_size(gpu, qd, kd, batch):
+    """Batches at the LDS sequence table's size and one past it (the instantiation that reads the indptrs
+    from memory), with one sequence whose length differs at the end of the batch so that the uniformity
+    scan past the table decides the split."""
+    rng = np.random.default_rng(3400 + batch)
+    lens = rng.integers(1, 120, size=batch).tolist()
+    spec = synth.CaseSpec(batch=batch, q_dtype=qd, kv_dtype=kd, lengths=lens, permuted=True, seed=3400 + batch)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units in (48, 256):
+        out = dc.run(num_units=units, min_chunk=32)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"table edge {qd}/{kd} b{batch} u{units}")
+    # equal lengths but the last: only the scan reaches it past a full table
+    lens = [1024] * (batch - 1) + [1000]
+    spec = synth.CaseSpec(batch=batch, q_dtype=qd, kv_dtype=kd, lengths=lens, seed=3401 + batch)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    dec = dc.decoder(num_units=256, min_chunk=32)
+    out = dc.run(dec)
+    torch.cuda.synchronize()
+    assert split_record(dec) == expected_split(case, 256, 32)
+    seqs = [0, batch // 2, batch - 2, batch - 1]
+    assert_parity(oracle_ref(case, sequences=seqs)[seqs], to64(out)[seqs], f"table edge long {qd}/{kd} b{batch}")
+
+
 def split_record(dec: binding.Decoder) -> list:
     """The split (base, cost, total, chunk, shares) the last attention launch recorded in the workspace."""
     words = dec.workspace.view(torch.int32)
