@@ -893,6 +893,11 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
           qb[q][s] = *reinterpret_cast<const bf16x8_t*>(row + d0 * 2);
         else
           q8[q][s] = *reinterpret_cast<const uint64_t*>(row + d0);
+        // two tokens of bf16 Q (144 registers): Q lives in the accumulation
+        // registers, which the products read directly (held in the vector
+        // registers, it would be spilled there and copied back before every
+        // product).  fp8 Q (72 registers) fits in the vector registers.
+        if constexpr (QL > 1 && QT == Dt::BF16) asm volatile("" : "+a"(qb[q][s]));
       }
     }
   } else {
