@@ -33,8 +33,9 @@
 //      and publishes them;
 //   4. after a second barrier computes O^T += V^T . P^T for its own 128 of the
 //      512 output columns over all 64 rows.  V's rows must sit along the MFMA
-//      K axis, so each lane reads 8-byte runs of 8 rows from LDS and
-//      interleaves them with v_perm while widening fp8 to bf16 (exact).
+//      K axis: each lane reads 8-row runs from LDS and interleaves them with
+//      v_perm (widening fp8 to bf16, exact), or, for fp8 V in the register
+//      ring, gets them from transposed reads (ds_read_b64_tr_b8).
 // The waves own disjoint output columns, so finishing a piece only needs the
 // per-head row sums of the 4 waves.
 #pragma once
@@ -77,7 +78,7 @@ struct KvLayout<Dt::FP8> {
   static constexpr int kRowBytes = 576;
   static constexpr int kChunks = 9;
   static constexpr int kVChunks = 8;
-  static constexpr int kVPitch = 544;  // LDS bytes per V row: 136 dwords, rows 4 apart land 32 banks apart
+  static constexpr int kVPitch = 528;  // LDS bytes per V row: 132 dwords, so row R starts 4R banks along
   static constexpr int kDepth = 3;     // tiles in flight per wave
 };
 
@@ -313,6 +314,17 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t d0, uint32_t d1) {
   r[2] = fp8x2_to_bf16x2(d1, false);
   r[3] = fp8x2_to_bf16x2(d1, true);
   return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// LDS read with an 8-bit transpose within each 16-lane group: lane
+// 8h + i of the group receives, as byte e, byte i of the 8 bytes addressed by
+// lane 2e + h of the group.  With the 16 lanes addressing 8 rows x two 8-byte
+// column halves of a matrix, each lane gets one column over the 8 rows: the
+// k-contiguous operand layout of a product whose k index runs over rows.
+__device__ __forceinline__ u32x2_t lds_read_tr8(const uint8_t* p) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+  return u32x2_t{(uint32_t)r[0], (uint32_t)r[1]};
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -969,7 +981,8 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // for every token of the pass (the V operands are built once).
   // k-step ks covers rows 32ks..32ks+31; slot s of lane group g is row
   // R = 32ks + (s/4)*16 + g*4 + s%4, which is wave 2ks + s/4's row g*4 + s%4.
-  // Block jb holds columns 128w + m*8 + jb, m = 0..15; lane c16 feeds m = c16.
+  // Block jb holds columns 128w + 16 jb + m (register ring, fp8 KV) or
+  // 128w + 8m + jb, m = 0..15; lane c16 feeds m = c16.
   // LDS ring: the next P.V's operands, read from LDS ahead of it (V of the
   // tile, still in its slot, right after the previous P.V; its weights right
   // after the barrier that publishes them), so that the next step's products
@@ -991,6 +1004,13 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         }
     }
   };
+  // Register ring, fp8 V: for k-step ks and column block jb (the wave's columns
+  // 16 jb .. 16 jb + 15) lane (c16, g) needs column 16 jb + c16 over the rows
+  // R(ks, g, s), s < 8, in the P operand's order.  One transposed read gives
+  // exactly that when lane (c16, g) addresses row R(ks, g, c16 / 2), columns
+  // 16 jb + 8 (c16 & 1) .. + 7.  (In the LDS ring the same reads, through the
+  // chunk swizzle, made the launch ~25% slower.)
+  [[maybe_unused]] const int v_row = 16 * (c16 >> 3) + 4 * g + ((c16 >> 1) & 3);  // R(0, g, c16 / 2)
   auto load_p = [&](int tt) {
     if constexpr (kLds) {
 #pragma unroll
@@ -1025,18 +1045,25 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         pp[3] = p1[1];
         pop[q] = __builtin_bit_cast(bf16x8_t, pp);
       }
-      if constexpr (KT == Dt::FP8) {
+      if constexpr (KT == Dt::FP8 && !kLds) {
+        // column block jb: one transposed read, widened to bf16, one product per token
         u32x2_t rv[8];
-        if constexpr (kLds) {
+        const uint8_t* vb = &sm.v[buf][v_row + 32 * ks][kColsPerWave * w + ((c16 & 1) << 3)];
 #pragma unroll
-          for (int sl = 0; sl < 8; ++sl) rv[sl] = vreg[ks][sl];
-        } else {
+        for (int jb = 0; jb < 8; ++jb) rv[jb] = lds_read_tr8(vb + 16 * jb);
 #pragma unroll
-          for (int sl = 0; sl < 8; ++sl) {
-            const int R = 32 * ks + (sl >> 2) * 16 + g * 4 + (sl & 3);
-            rv[sl] = *reinterpret_cast<const u32x2_t*>(&sm.v[buf][R][kColsPerWave * w + c16 * 8]);
-          }
+        for (int jb = 0; jb < 8; ++jb) {
+          const bf16x8_t op = fp8x8_to_bf16x8(rv[jb][0], rv[jb][1]);
+#pragma unroll
+          for (int q = 0; q < QL; ++q)
+            acc[q][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, pop[q], acc[q][jb], 0, 0, 0);
         }
+      } else if constexpr (KT == Dt::FP8) {
+        // LDS ring: 8-byte runs of 8 rows (read by load_v), interleaved with
+        // v_perm while widening
+        u32x2_t rv[8];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) rv[sl] = vreg[ks][sl];
 #pragma unroll
         for (int wd = 0; wd < 2; ++wd) {
           u32x4_t op[4];
@@ -1366,14 +1393,13 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   if constexpr (kLds) wait_vm<0>();  // no tile load may still land in the staging slot
   __syncthreads();
   // Lane (c16, g) holds, for block jb and i < 4, head c16 at column
-  // 128w + (4g+i)*8 + jb: a contiguous run of 32 columns.  Written straight
-  // from there, every store instruction puts 16 bytes into each of 64
-  // different lines.  With one token per pass each wave stages its rows in LDS
-  // instead (the V buffers are free once the last P.V is done) and reads them
-  // back so that every store covers whole runs of the wave's 128 columns of 2
-  // heads (float32) or 4 heads (bf16); reads follow the same wave's writes in
-  // issue order.  Two-token passes have no registers to spare and store
-  // directly.
+  // 128w + 16 jb + 4g + i (register ring, fp8 KV: four neighbouring columns
+  // per block) or 128w + (4g+i)*8 + jb (a contiguous run of 32 columns).  With one
+  // token per pass each wave stages its rows in LDS (the V buffers are free
+  // once the last P.V is done) and reads them back so that every store covers
+  // whole runs of the wave's 128 columns of 2 heads (float32) or 4 heads
+  // (bf16); reads follow the same wave's writes in issue order.  Two-token
+  // passes have no registers to spare and store directly.
   uint8_t* const stage = sm.out_stage() + (size_t)w * kOutStageBytes;
 #pragma unroll
   for (int q = 0; q < QL; ++q) {
@@ -1382,25 +1408,17 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     const float scale = Lsum > 0.f ? out_mul / Lsum : 0.f;
     const int t = pc.t0 + q;
     if constexpr (QL > 1) {
+      static_assert(KT == Dt::FP8, "two tokens per pass are for fp8 KV");
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = kColsPerWave * w + (4 * g + i) * 8;
+      for (int jb = 0; jb < 8; ++jb) {
+        const int col = kColsPerWave * w + 16 * jb + 4 * g;
         if (pc.complete) {
-          u32x4_t pk;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(acc[q][2 * u][i] * scale, acc[q][2 * u + 1][i] * scale);
-          *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
+          const u32x2_t pk{pack_bf16x2(acc[q][jb][0] * scale, acc[q][jb][1] * scale),
+                           pack_bf16x2(acc[q][jb][2] * scale, acc[q][jb][3] * scale)};
+          *reinterpret_cast<u32x2_t*>(a.out + ((size_t)t * kHeads + c16) * kVDim + col) = pk;
         } else {
-          f32x4_t v0, v1;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            v0[u] = acc[q][u][i] * scale;
-            v1[u] = acc[q][4 + u][i] * scale;
-          }
-          f32x4_t* dst =
-              reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + c16) * kVDim + col);
-          dst[0] = v0;
-          dst[1] = v1;
+          *reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + c16) * kVDim + col) =
+              acc[q][jb] * scale;
         }
       }
     } else if (pc.complete) {
