@@ -843,6 +843,13 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     const int nchunks = src16 ? kChunks16 : kChunks16 / 2;
     const int per_head = src16 ? kQKDim * 2 / 16 : kQKDim / 16;  // 72 or 36
     u32x4_t stage[QL][kPer];
+    // LDS ring: the ring's page indices are in before anything else goes out.
+    // For the first piece they were requested before the start's barriers and
+    // have long arrived; a later piece needs them for its first tile anyway.
+    // Without this wait the compiler, joining the two paths, cannot count
+    // which loads the second tile's indices are behind and waits for all of
+    // them, the first tile's own loads included (a whole round trip).
+    if constexpr (kLds) wait_vm<0>();
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) +
@@ -858,6 +865,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         stage[q][i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)c * 16);
       }
     }
+    if constexpr (kLds) __builtin_amdgcn_sched_barrier(0);  // every Q load before the tiles' loads
     if constexpr (kLds) {
       // tiles 0 and 1 now (ring.first[j] becomes the page of the next tile
       // slot j receives: 4 and 5); tile 2 goes out during the first step's
@@ -870,6 +878,8 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         ring.first[k] = piece_page(a.kv_indices, pc.ip0, pc.nrows, (k + kSlots) * kTileRows + my_row, sh);
       }
       pend = dma_rows(page_row(ring.first[2], pc.nrows, 2 * kTileRows + my_row, sh), dl);
+      // Q is in (behind it: the two tiles' loads and two page loads)
+      wait_vm<2 * kTileOps>();
     } else {
       issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
     }
