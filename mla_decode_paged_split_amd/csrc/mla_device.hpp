@@ -834,24 +834,57 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     // Q goes through LDS: the workgroup loads each token's 16 rows once (16-byte
     // pieces over all 256 threads) instead of every wave loading all of them,
     // so 4x fewer requests sit in front of the tiles.  Order: Q loads, the
-    // first three tiles (slots 0..2), then Q into LDS slot 3 (cast to fp8
-    // there when fp8 Q is given as bf16), a barrier once tile 0 has landed,
-    // and each wave's fragments from LDS.
+    // first tiles, then (register ring) Q into LDS (cast to fp8 there when
+    // fp8 Q is given as bf16), a barrier once tile 0 has landed, and each
+    // wave's fragments from LDS.
     const bool src16 = (QT == Dt::BF16) || a.q_cast;  // the source holds bf16 values
     constexpr int kChunks16 = kHeads * kQKDim * 2 / 16;  // 1152 sixteen-byte pieces of a bf16 Q token
     constexpr int kPer = (kChunks16 + kThreads - 1) / kThreads;  // 5
     const int nchunks = src16 ? kChunks16 : kChunks16 / 2;
     const int per_head = src16 ? kQKDim * 2 / 16 : kQKDim / 16;  // 72 or 36
-    u32x4_t stage[QL][kPer];
-    // LDS ring: the ring's page indices are in before anything else goes out.
-    // For the first piece they were requested before the start's barriers and
-    // have long arrived; a later piece needs them for its first tile anyway.
-    // Without this wait the compiler, joining the two paths, cannot count
-    // which loads the second tile's indices are behind and waits for all of
-    // them, the first tile's own loads included (a whole round trip).
-    if constexpr (kLds) wait_vm<0>();
+    [[maybe_unused]] u32x4_t stage[QL][kPer];
+    if constexpr (kLds) {
+      // The ring's page indices are in before anything else goes out.  For
+      // the first piece they were requested before the start's barriers and
+      // have long arrived; a later piece needs them for its first tile
+      // anyway.  Without this wait the compiler, joining the two paths,
+      // cannot count which loads the second tile's indices are behind and
+      // waits for all of them, the first tile's own loads included.
+      wait_vm<0>();
+    }
+    // bf16 Q in the LDS ring: straight into LDS slot 3 with direct-to-LDS
+    // loads, so that no register has to wait for it behind the tiles' loads
+    // (a store of loaded Q to LDS after them makes the compiler wait for
+    // every tile load, tile 1's included: the first step would start only
+    // once tiles 0 and 1 are in).  Staging chunk p (16 bytes) is column
+    // p % 73 of head row p / 73 (1168-byte pitch); columns past the row's end
+    // and rows past the 16th fetch the row's last chunk and land in unused
+    // space of the slot.  fp8 Q keeps the register path (it is cast to fp8
+    // on the way when given as bf16; cast after a direct-to-LDS load, in
+    // LDS, it came out 0.4 us slower on the 64 x 8192 batch).
+    constexpr bool kQDma = kLds && QT == Dt::BF16;
+    if constexpr (kQDma) {
+      constexpr int kQPitchChunks = kQPitch / 16;                                       // 73
+      constexpr int kQDmaOps = (kHeads * kQPitchChunks + kThreads - 1) / kThreads;      // 5 per wave
+      static_assert(kQDmaOps * kThreads * 16 <= kTileRows * kF8Row, "Q staging fits a slot");
+      constexpr int ncol = kQKDim * 2 / 16;  // 72 chunks per head row
+      const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q) + (size_t)pc.t0 * kHeads * kQKDim * 2;
+      const int wq = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+      for (int ii = 0; ii < kQDmaOps; ++ii) {
+        const int j = ii * kWaves + wq;  // this wave's 1 KB of the staging
+        const int pch = j * 64 + lane;
+        const int row = min(pch / kQPitchChunks, kHeads - 1);
+        const int col = min(pch - (pch / kQPitchChunks) * kQPitchChunks, ncol - 1);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(qsrc + (size_t)row * ncol * 16 + col * 16),
+            reinterpret_cast<__attribute__((address_space(3))) void*>((uintptr_t)(sm.q_stage() + j * 1024)), 16,
+            0, 0);
+      }
+    }
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
+      if constexpr (kQDma) break;
       const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) +
                            (size_t)(pc.t0 + (q < pc.ntok ? q : 0)) * kHeads * kQKDim * (src16 ? 2 : 1);
       // every thread issues all kPer loads (index clamped; surplus ones are not
@@ -865,7 +898,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         stage[q][i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)c * 16);
       }
     }
-    if constexpr (kLds) __builtin_amdgcn_sched_barrier(0);  // every Q load before the tiles' loads
+    if constexpr (kLds && !kQDma) __builtin_amdgcn_sched_barrier(0);  // every Q load before the tiles' loads
     if constexpr (kLds) {
       // tiles 0 and 1 now (ring.first[j] becomes the page of the next tile
       // slot j receives: 4 and 5); tile 2 goes out during the first step's
@@ -879,12 +912,13 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       }
       pend = dma_rows(page_row(ring.first[2], pc.nrows, 2 * kTileRows + my_row, sh), dl);
       // Q is in (behind it: the two tiles' loads and two page loads)
-      wait_vm<2 * kTileOps>();
+      if constexpr (!kQDma) wait_vm<2 * kTileOps>();
     } else {
       issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
     }
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
+      if constexpr (kQDma) break;  // staged by its direct-to-LDS loads
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int c = threadIdx.x + i * kThreads;
@@ -900,7 +934,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       }
     }
     if constexpr (kLds) {
-      wait_vm<kTileOps + 1>();  // tile 0 is in LDS (after it: tile 1's loads and two page loads)
+      wait_vm<kTileOps + 1>();  // Q and tile 0 are in LDS (after them: tile 1's loads and two page loads)
       lds_barrier();
     } else {
       __syncthreads();
