@@ -1566,6 +1566,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   // before the ring's indices can be requested)
   const int32_t ip_first = a.kv_indptr[0];
   const int32_t ip_last = a.kv_indptr[a.batch];
+  // The two float arguments are first used after the start's barriers; read
+  // there, their scalar load (and its wait) went out only then, on the path
+  // to the first tile.  Read now, it overlaps the first round trip.
+  const float sm_scale = a.sm_scale;
+  const float logit_cap = a.logit_cap;
+  asm volatile("" ::"s"(sm_scale), "s"(logit_cap));
   // these loads go out before the ring's, so using them never waits for the ring's indices
   __builtin_amdgcn_sched_barrier(0);
   // LDS ring: the per-lane constants of the tile loads, computed while the
@@ -1637,11 +1643,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
   const int lo = k * geo.chunk;
   const int hi = min(lo + geo.chunk, geo.total);
 
-  const float c_nat = a.sm_scale * qs * ks;
+  const float c_nat = sm_scale * qs * ks;
   Logit logit;
   logit.c_score = c_nat * kLog2e;
-  logit.k1 = kCap ? 2.0f * kLog2e * c_nat / a.logit_cap : 0.f;
-  logit.k2 = a.logit_cap * kLog2e;
+  logit.k1 = kCap ? 2.0f * kLog2e * c_nat / logit_cap : 0.f;
+  logit.k2 = logit_cap * kLog2e;
   const float out_mul = ks;
 
   const bool primed = geo.cost == 0;  // the ring's indices above are the first piece's
