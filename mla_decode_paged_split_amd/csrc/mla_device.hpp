@@ -810,12 +810,13 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   using L = KvLayout<KT>;
   constexpr int D = RingT::D;
   constexpr bool kLds = lds_ring<KT, QL>();
-  const int lane = threadIdx.x & 63;
+  // (not const: the LDS ring re-derives them once the first tiles' loads are out)
+  int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int c16 = lane & 15;
-  const int g = lane >> 4;
+  int c16 = lane & 15;
+  int g = lane >> 4;
   const int sh = kGeneral ? a.page_shift : 0;
-  const int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
+  int my_row = 16 * w + c16;  // this lane's row within a tile (for loads)
   // LDS ring: the rows of the tile whose loads the next step issues (dl: the
   // per-lane constants of the tile loads), this wave's 16 rows in a slot (the
   // wave index made a scalar once) and the next S^T's K fragments
@@ -913,6 +914,16 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
       pend = dma_rows(page_row(ring.first[2], pc.nrows, 2 * kTileRows + my_row, sh), dl);
       // Q is in (behind it: the two tiles' loads and two page loads)
       if constexpr (!kQDma) wait_vm<2 * kTileOps>();
+      // The lane indices again, from a copy the compiler cannot see through:
+      // the per-lane addresses of the steps that follow derive from them, and
+      // would otherwise be computed once before the piece loop, on the way to
+      // these loads; now they are computed while the loads fly.
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      lane = tid & 63;
+      c16 = lane & 15;
+      g = lane >> 4;
+      my_row = 16 * w + c16;
     } else {
       issue_ring_rows<KT>(a.kv, pc.nrows, sh, ring);
     }
