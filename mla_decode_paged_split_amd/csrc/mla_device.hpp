@@ -1454,7 +1454,8 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
   // once the last P.V is done) and reads them back so that every store covers
   // whole runs of the wave's 128 columns of 2 heads (float32) or 4 heads
   // (bf16); reads follow the same wave's writes in issue order.  Two-token
-  // passes have no registers to spare and store directly.
+  // passes of fp8 Q stage one token after the other; those of bf16 Q store
+  // straight from the registers.
   uint8_t* const stage = sm.out_stage() + (size_t)w * kOutStageBytes;
 #pragma unroll
   for (int q = 0; q < QL; ++q) {
@@ -1462,7 +1463,9 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     const float Lsum = sm.lsum[0][q][c16] + sm.lsum[1][q][c16] + sm.lsum[2][q][c16] + sm.lsum[3][q][c16];
     const float scale = Lsum > 0.f ? out_mul / Lsum : 0.f;
     const int t = pc.t0 + q;
-    if constexpr (QL > 1) {
+    if constexpr (QL > 1 && QT == Dt::BF16) {
+      // two tokens of bf16 Q: stored straight from the registers (staging
+      // them spilled)
       static_assert(KT == Dt::FP8, "two tokens per pass are for fp8 KV");
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) {
@@ -1476,6 +1479,40 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
               acc[q][jb] * scale;
         }
       }
+    } else if constexpr (QL > 1) {
+      // staged like one token, token by token (each wave reuses its area once
+      // its own reads of the previous token are done: LDS operations of one
+      // wave complete in order)
+      static_assert(KT == Dt::FP8, "two tokens per pass are for fp8 KV");
+      if (pc.complete) {
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) {
+          const u32x2_t pk{pack_bf16x2(acc[q][jb][0] * scale, acc[q][jb][1] * scale),
+                           pack_bf16x2(acc[q][jb][2] * scale, acc[q][jb][3] * scale)};
+          *reinterpret_cast<u32x2_t*>(stage + c16 * kOutPitchBf16 + (16 * jb + 4 * g) * 2) = pk;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r = 0; r < kHeads / 4; ++r) {
+          const int h = 4 * r + (lane >> 4);
+          const int c = lane & 15;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + h * kOutPitchBf16 + c * 16);
+          st_stream(v, a.out + ((size_t)t * kHeads + h) * kVDim + kColsPerWave * w + c * 8);
+        }
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+          *reinterpret_cast<f32x4_t*>(stage + c16 * kOutPitchF32 + (16 * jb + 4 * g) * 4) = acc[q][jb] * scale;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r = 0; r < kHeads / 2; ++r) {
+          const int h = 2 * r + (lane >> 5);
+          const int c = lane & 31;
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + h * kOutPitchF32 + c * 16);
+          st_stream(v, a.part_o + ((size_t)(pc.slot + q) * kHeads + h) * kVDim + kColsPerWave * w + c * 4);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     } else if (pc.complete) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
