@@ -771,6 +771,7 @@ struct Piece {
   int lim[QL];    // rows (from the piece start) token j sees: <= nrows, <= 0 for none
   int slot;       // partial row of token j is slot + j (unused when complete)
   bool complete;  // the piece is the whole sequence: write bf16 rows
+  bool last;      // no other pass follows in this workgroup (one token: stream the results out)
 };
 
 // Score transform, raw dot product -> log2-domain logit: sc * c_score, or
@@ -1522,12 +1523,31 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         *reinterpret_cast<u32x4_t*>(stage + c16 * kOutPitchBf16 + (4 * g + i) * 16) = pk;
       }
       __builtin_amdgcn_wave_barrier();
+      // The last pass of a workgroup streams its rows out (non-temporal: no
+      // line stays dirty in the L2 for the write-back at the launch's end).
+      // A pass that another follows stores them plainly: the next pass's first
+      // waits count these stores too (the vector-memory count covers loads and
+      // stores in issue order), and a plain store completes in the L2, a
+      // streamed one only in memory.  The empty asm statements keep the
+      // compiler from folding the two loops into one, which drops the hint.
+      if (pc.last) {
 #pragma unroll
-      for (int r = 0; r < kHeads / 4; ++r) {
-        const int h = 4 * r + (lane >> 4);
-        const int c = lane & 15;  // 16-byte piece of the head's 256 bytes
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + h * kOutPitchBf16 + c * 16);
-        st_stream(v, a.out + ((size_t)t * kHeads + h) * kVDim + kColsPerWave * w + c * 8);
+        for (int r = 0; r < kHeads / 4; ++r) {
+          const int h = 4 * r + (lane >> 4);
+          const int c = lane & 15;  // 16-byte piece of the head's 256 bytes
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + h * kOutPitchBf16 + c * 16);
+          st_stream(v, a.out + ((size_t)t * kHeads + h) * kVDim + kColsPerWave * w + c * 8);
+        }
+      } else {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < kHeads / 4; ++r) {
+          const int h = 4 * r + (lane >> 4);
+          const int c = lane & 15;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + h * kOutPitchBf16 + c * 16);
+          *reinterpret_cast<u32x4_t*>(a.out + ((size_t)t * kHeads + h) * kVDim + kColsPerWave * w + c * 8) = v;
+        }
+        asm volatile("" ::: "memory");
       }
     } else {
 #pragma unroll
@@ -1543,12 +1563,25 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         dst[1] = v1;
       }
       __builtin_amdgcn_wave_barrier();
+      if (pc.last) {  // streamed or plain, as for the bf16 rows above
 #pragma unroll
-      for (int r = 0; r < kHeads / 2; ++r) {
-        const int h = 2 * r + (lane >> 5);
-        const int c = lane & 31;  // 16-byte piece of the head's 512 bytes
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + h * kOutPitchF32 + c * 16);
-        st_stream(v, a.part_o + ((size_t)(pc.slot + q) * kHeads + h) * kVDim + kColsPerWave * w + c * 4);
+        for (int r = 0; r < kHeads / 2; ++r) {
+          const int h = 2 * r + (lane >> 5);
+          const int c = lane & 31;  // 16-byte piece of the head's 512 bytes
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + h * kOutPitchF32 + c * 16);
+          st_stream(v, a.part_o + ((size_t)(pc.slot + q) * kHeads + h) * kVDim + kColsPerWave * w + c * 4);
+        }
+      } else {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < kHeads / 2; ++r) {
+          const int h = 2 * r + (lane >> 5);
+          const int c = lane & 31;
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + h * kOutPitchF32 + c * 16);
+          *reinterpret_cast<f32x4_t*>(a.part_o + ((size_t)(pc.slot + q) * kHeads + h) * kVDim + kColsPerWave * w +
+                                      c * 4) = v;
+        }
+        asm volatile("" ::: "memory");
       }
     }
     if (w == 0 && g == 0) {
@@ -1765,6 +1798,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
       }
       pc.slot = complete ? -1 : slot * a.max_q_len + tau0;
       pc.complete = complete;
+      pc.last = b == bmax && tau0 + QL >= q_len;
       if (!primed || b != bmin || tau0 != 0) issue_ring_indices(a.kv_indices, pc.ip0, nrows, sh, ring);
       attend_piece<QT, KT, QL, kGeneral, kCap>(a, sm, pc, logit, out_mul, ring, dl);
     }
