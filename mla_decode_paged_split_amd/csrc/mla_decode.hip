@@ -128,15 +128,13 @@ hipError_t launch_attention_general(const mla::Args& a, hipStream_t stream) {
 
 // The plain decode (pages of one row, one token per sequence, no soft-cap)
 // runs a kernel with the page arithmetic and the cap compiled out.  Otherwise
-// fp8 KV serves two tokens per walk of a piece and bf16 KV (twice the row
-// bytes in the register ring) walks a piece once per token, in a form with
-// the cap compiled in or out.
+// a kernel with the cap compiled in or out serves one token per walk of a
+// piece, or two when some sequence has several.
 template <mla::Dt QT, mla::Dt KT>
 hipError_t launch_attention(const mla::Args& a, hipStream_t stream) {
   const bool general = a.page_shift > 0 || a.max_q_len > 1 || a.logit_cap > 0.f;
   if (!general) return launch_attention_ql<QT, KT, 1, 0>(a, stream);
-  if constexpr (KT == mla::Dt::FP8)
-    if (a.max_q_len > 1) return launch_attention_general<QT, KT, 2>(a, stream);
+  if (a.max_q_len > 1) return launch_attention_general<QT, KT, 2>(a, stream);
   return launch_attention_general<QT, KT, 1>(a, stream);
 }
 

@@ -613,7 +613,8 @@ __device__ __forceinline__ int page_row(int page, int nrows, int pr, int sh) {
 // walk is bound by its arithmetic rather than by memory, and the registers a
 // deeper ring holds serve the compiler's schedule better (fp8 Q: 1.3 us
 // shorter on a 64 x 8192 batch with a ring of two tiles than of three; bf16 Q
-// needs the room for its second token's 72 registers of Q).
+// needs the room for its second token's 72 registers of Q).  Over bf16 KV
+// that leaves one tile of 72 registers (a second one spilled).
 template <Dt QT, Dt KT, int QL>
 constexpr int ring_depth() {
   return QL > 1 ? KvLayout<KT>::kDepth - 1 : KvLayout<KT>::kDepth;
@@ -1464,10 +1465,9 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
     const float Lsum = sm.lsum[0][q][c16] + sm.lsum[1][q][c16] + sm.lsum[2][q][c16] + sm.lsum[3][q][c16];
     const float scale = Lsum > 0.f ? out_mul / Lsum : 0.f;
     const int t = pc.t0 + q;
-    if constexpr (QL > 1 && QT == Dt::BF16) {
+    if constexpr (QL > 1 && QT == Dt::BF16 && KT == Dt::FP8) {
       // two tokens of bf16 Q: stored straight from the registers (staging
       // them spilled)
-      static_assert(KT == Dt::FP8, "two tokens per pass are for fp8 KV");
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) {
         const int col = kColsPerWave * w + 16 * jb + 4 * g;
@@ -1480,11 +1480,10 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
               acc[q][jb] * scale;
         }
       }
-    } else if constexpr (QL > 1) {
+    } else if constexpr (QL > 1 && KT == Dt::FP8) {
       // staged like one token, token by token (each wave reuses its area once
       // its own reads of the previous token are done: LDS operations of one
       // wave complete in order)
-      static_assert(KT == Dt::FP8, "two tokens per pass are for fp8 KV");
       if (pc.complete) {
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb) {
@@ -1584,6 +1583,7 @@ __device__ void attend_piece(const Args& a, Smem<KT, QL>& sm, const Piece<QL>& p
         asm volatile("" ::: "memory");
       }
     }
+    if constexpr (QL > 1 && KT == Dt::BF16) __builtin_amdgcn_wave_barrier();  // the next token reuses the area
     if (w == 0 && g == 0) {
       // no visible row: -inf (no weight in a merge); a NaN sum (NaN inputs) stays NaN so that it
       // propagates through the merge as it does through an unsplit sequence

@@ -189,6 +189,9 @@ FEATURE_WORKLOADS = {
         {"causal": True}),
     "f4_cap30_bf16q_fp8kv_b64_kv8192": (
         CaseSpec(batch=64, q_dtype="bf16", kv_dtype="fp8", kv_len=8192, seed=6000), {"logit_cap": 30.0}),
+    "f3_mtp2_causal_bf16_b64_kv8192": (
+        CaseSpec(batch=64, q_dtype="bf16", kv_dtype="bf16", kv_len=8192, q_lens=[2] * 64, seed=7100),
+        {"causal": True}),
 }
 
 
