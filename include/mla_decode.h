@@ -151,8 +151,10 @@ typedef struct {
   int32_t reserved;
   uint64_t off_counters; /* int32 [batch]: arrivals per split sequence (fused merge), left at 0 after each
                             run; then 8 int32: the split of the last attention launch, for the merge */
-  uint64_t off_part_o;   /* float32 [2 * num_units * max_q_len, 16, 512]: normalised split partials */
-  uint64_t off_part_lse; /* float32 [2 * num_units * max_q_len, 16]: log2-sum-exp of each partial */
+  uint64_t off_part_o;   /* float32 [(2 * num_units + batch * S) * max_q_len, 16, 512]: normalised split
+                            partials; S = num_units / batch if that is 2 to 8, else 0: slots per
+                            sequence that the merge loads before it reads the split */
+  uint64_t off_part_lse; /* float32 [(2 * num_units + batch * S) * max_q_len, 16]: log2-sum-exp of each */
 } mla_decode_plan_t;
 
 /*
@@ -250,9 +252,9 @@ mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, co
  * ends.  params are validated and resolved as mla_decode_plan does (against
  * the current device; `stream` must belong to it); a problem whose
  * workspace would exceed the array (mla_decode_workspace_size(params) >
- * MLA_NOALLOC_SCRATCH_BYTES: e.g. more than 256 workgroup shares with one
- * query token, or more than 128 with two) is MLA_ERR_WORKSPACE, before any
- * launch.  The first call on a device looks up the array's device address
+ * MLA_NOALLOC_SCRATCH_BYTES; the array holds the partials of 256 workgroup
+ * shares with one query token, or 128 with two, at any batch) is
+ * MLA_ERR_WORKSPACE, before any launch.  The first call on a device looks up the array's device address
  * (no allocation).  Every call on one device shares the array, so calls
  * that may overlap in time on one device (two streams, two threads) race
  * and must not be issued; calls in one stream are ordered.  With
@@ -260,7 +262,7 @@ mla_status mla_decode_run_paged(const mla_decode_plan_t* plan, const void* q, co
  * small fill kernel.  Other arguments, layouts and errors as for
  * mla_decode_run_paged.
  */
-#define MLA_NOALLOC_SCRATCH_BYTES (18u << 20)
+#define MLA_NOALLOC_SCRATCH_BYTES (26u << 20)
 mla_status mla_decode_run_noalloc(const mla_decode_params* params, const void* q, const void* kv,
                                   const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                                   const int32_t* kv_last_page_len, const float* q_scale, const float* kv_scale,

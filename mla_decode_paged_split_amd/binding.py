@@ -61,7 +61,7 @@ MLA_FLAG_FUSED_MERGE = 1
 MLA_FLAG_FUSED_Q_CAST = 2
 MLA_FLAG_CAUSAL = 4
 MLA_QUANT_DYNAMIC_SCRATCH_BYTES = 1024
-MLA_NOALLOC_SCRATCH_BYTES = 18 << 20
+MLA_NOALLOC_SCRATCH_BYTES = 26 << 20
 
 _DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3FN}
 

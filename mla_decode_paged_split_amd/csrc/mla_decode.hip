@@ -76,9 +76,20 @@ struct Layout {
 
 int32_t max_q_of(const mla_decode_params* p) { return p->max_q_len > 0 ? p->max_q_len : 1; }
 
-// Partials: two slots per workgroup share, each with a row per query token.
+// Partial slots of their own per sequence (mla::part_slot): as many as a
+// sequence has pieces when every sequence has the same length, where that is
+// 2 to mla::kMaxSpec; else none (a sequence with more pieces than the merge
+// loads ahead gains nothing from the slots).
+int32_t spec_of(const mla_decode_params* p, int32_t units) {
+  if ((int64_t)units < 2 * (int64_t)p->batch) return 0;
+  const int32_t s = units / p->batch;
+  return s <= mla::kMaxSpec ? s : 0;
+}
+
+// Partials: spec slots per sequence, then two per workgroup share, each with
+// a row per query token.
 Layout layout_for(const mla_decode_params* p, int32_t units) {
-  const size_t slots = (size_t)2 * units * max_q_of(p);
+  const size_t slots = ((size_t)2 * units + (size_t)p->batch * spec_of(p, units)) * max_q_of(p);
   Layout L;
   L.counters = 0;
   L.part_o = align_up(((size_t)p->batch + mla::kGeoWords) * sizeof(int32_t));
@@ -175,6 +186,7 @@ mla_status make_args(const mla_decode_plan_t* plan, const int32_t* qo_indptr, co
   a->causal = (p.flags & MLA_FLAG_CAUSAL) ? 1 : 0;
   a->fused = (p.flags & MLA_FLAG_FUSED_MERGE) ? 1 : 0;
   a->q_cast = (p.flags & MLA_FLAG_FUSED_Q_CAST) ? 1 : 0;
+  a->spec = spec_of(&p, p.num_units);
   return MLA_OK;
 }
 

@@ -192,8 +192,8 @@ struct Args {
   float logit_cap;    // 0: off
   uint16_t* out;      // bf16 bits [total_q, 16, 512]
   float* lse_out;     // [total_q, 16] natural-log sum-exp of each token's scores, or null
-  float* part_o;      // [2*units*max_q_len, 16, 512]
-  float* part_lse;    // [2*units*max_q_len, 16], log2 domain
+  float* part_o;      // [(2*units + batch*spec) * max_q_len, 16, 512]
+  float* part_lse;    // [(2*units + batch*spec) * max_q_len, 16], log2 domain
   int32_t* counters;  // [batch] arrivals, then kGeoWords words: the split of the last attention launch
   int32_t batch;
   int32_t units;
@@ -203,6 +203,7 @@ struct Args {
   int32_t causal;
   int32_t fused;
   int32_t q_cast;  // fp8 Q given as bf16: cast in the kernel (same rounding as mla_quantize_q_kernel)
+  int32_t spec;    // pieces per sequence with partial slots of their own (0..kMaxSpec, see part_slot)
 };
 
 // ------------------------------------------------------------------ helpers
@@ -496,8 +497,26 @@ __device__ __forceinline__ int piece_count(int st, int en, int chunk) {
   return (en - 1) / chunk - st / chunk + 1;
 }
 
+// Partial slot of piece i of sequence b.  The first `spec` pieces of every
+// sequence have slots of their own, b * spec + i, which the merge launch can
+// load before it has read the split (its first round trip); the others
+// follow them, in the slots of their workgroup shares (piece_slot).  The
+// library chooses spec = units / batch (the pieces of a sequence when every
+// sequence has the same length) where that is 2 to kMaxSpec, else 0.
+constexpr int kMaxSpec = 8;
+__device__ __forceinline__ int part_slot(int b, int i, int st, int chunk, int spec, int batch) {
+  return i < spec ? b * spec + i : batch * spec + piece_slot(st, chunk, i);
+}
+
 // ------------------------------------------------------------------- merge
 
+// Pieces 0..kMaxSpec-1 of one head, loaded by the merge launch before it knows
+// how many the sequence has: lane l's 8 columns of each, and lane i's lse of
+// piece i.
+struct MergePre {
+  f32x4_t a[kMaxSpec], b[kMaxSpec];
+  float lse;
+};
 
 // One wave merges the S partials of one head:
 //   out[h,:] = sum_i 2^(lse_i - M) o_i[h,:] / sum_i 2^(lse_i - M),  M = max_i lse_i,
@@ -511,27 +530,41 @@ __device__ __forceinline__ int piece_count(int st, int en, int chunk) {
 // a NaN lse (NaN inputs) gives a NaN weight and a NaN result.
 // With lse_dst, lane 0 also stores the merged natural-log sum-exp,
 // (M + log2 sum_i 2^(lse_i - M)) ln 2, or -inf when every piece is empty.
-template <class SlotFn>
+// kPre: all S <= kMaxSpec pieces are already loaded in *pre (same
+// arithmetic; a mix of loaded and preloaded pieces would join the two paths
+// on values still in flight, and the compiler waits for them there).
+template <bool kPre = false, class SlotFn>
 __device__ void merge_head_wave(const float* __restrict__ part_o, const float* __restrict__ part_lse, int S,
                                 SlotFn slot_of, float lse_mul, int h, uint16_t* __restrict__ out_head,
-                                float* __restrict__ lse_dst) {
+                                float* __restrict__ lse_dst, const MergePre* pre = nullptr) {
   const int lane = threadIdx.x & 63;
   constexpr int kBatch = 8;
+  static_assert(kBatch == kMaxSpec, "preloaded pieces fill the first batch");
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY;
   float wsum = 0.f;
   for (int i0 = 0; i0 < S; i0 += 64) {
     const int n = min(64, S - i0);
     f32x4_t a[kBatch], b[kBatch];
+    float v;
+    if constexpr (kPre) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (u < n) {
-        const f32x4_t* src =
-            reinterpret_cast<const f32x4_t*>(part_o + ((size_t)slot_of(i0 + u) * kHeads + h) * kVDim + lane * 8);
-        a[u] = src[0];
-        b[u] = src[1];
+      for (int u = 0; u < kBatch; ++u) {
+        a[u] = pre->a[u];
+        b[u] = pre->b[u];
       }
-    const float v = (lane < n) ? part_lse[slot_of(i0 + lane) * kHeads + h] * lse_mul : -INFINITY;
+      v = (lane < n) ? pre->lse * lse_mul : -INFINITY;
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (u < n) {
+          const f32x4_t* src =
+              reinterpret_cast<const f32x4_t*>(part_o + ((size_t)slot_of(i0 + u) * kHeads + h) * kVDim + lane * 8);
+          a[u] = src[0];
+          b[u] = src[1];
+        }
+      v = (lane < n) ? part_lse[slot_of(i0 + lane) * kHeads + h] * lse_mul : -INFINITY;
+    }
     const float m_new = fmaxf(M, wave_max(v));
     if (m_new != M) {  // rescale what earlier chunks accumulated (uniform across the wave)
       const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m_new);
@@ -1781,7 +1814,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
     const int s_lo = max(st, lo);
     const int s_hi = min(en, hi);
     const bool complete = (st >= lo) && (en <= hi);
-    const int slot = complete ? -1 : (st <= lo ? 2 * k : 2 * k + 1);
+    // this workgroup holds piece k - st / chunk of the sequence
+    const int slot = complete ? -1 : part_slot(b, k - st / geo.chunk, st, geo.chunk, a.spec, a.batch);
     const int r0 = (s_lo - st) << sh;  // the piece's first row within the sequence
     const int nrows = min((s_hi - st) << sh, n_rows) - r0;
     for (int tau0 = 0; tau0 < q_len; tau0 += QL) {
@@ -1812,12 +1846,15 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
         __threadfence();
         const int chunk = geo.chunk;
         const int qmax = a.max_q_len;
+        const int spec = a.spec;
+        const int batch = a.batch;
         const int w = threadIdx.x >> 6;
         for (int tau = 0; tau < q_len; ++tau)
           for (int hh = 0; hh < kHeads / kWaves; ++hh) {
             const int h = w * (kHeads / kWaves) + hh;
             merge_head_wave(
-                a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i) * qmax + tau; }, 1.0f, h,
+                a.part_o, a.part_lse, S,
+                [=](int i) { return part_slot(b, i, st, chunk, spec, batch) * qmax + tau; }, 1.0f, h,
                 a.out + ((size_t)(t + tau) * kHeads + h) * kVDim,
                 a.lse_out != nullptr ? a.lse_out + (size_t)(t + tau) * kHeads + h : nullptr);
           }
@@ -1859,7 +1896,28 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int b = blockIdx.x;
   const int h = blockIdx.y;
   const int tau = blockIdx.z;
-  // Every index this wave needs is loaded first, in one round trip: a load
+  const int lane = threadIdx.x & 63;
+  const int spec = a.spec;
+  const int qmax = a.max_q_len;
+  // The sequence's first `spec` pieces have slots that depend on b alone
+  // (part_slot): their loads go out with the first round trip below, before
+  // the split is known.  Slots past the sequence's pieces hold stale values
+  // and are never used.
+  MergePre pre;
+#pragma unroll
+  for (int u = 0; u < kMaxSpec; ++u) {
+    if (u < spec) {
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(
+          a.part_o + ((size_t)((b * spec + u) * qmax + tau) * kHeads + h) * kVDim + lane * 8);
+      pre.a[u] = src[0];
+      pre.b[u] = src[1];
+    } else {
+      pre.a[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pre.b[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  pre.lse = lane < spec ? a.part_lse[((b * spec + lane) * qmax + tau) * kHeads + h] : -INFINITY;
+  // Every index this wave needs is loaded in the same round trip: a load
   // written after one of the early exits below is issued only once the values
   // that decide the exit have arrived.
   const int32_t* gr = a.counters + a.batch;  // the split the attention launch used
@@ -1877,18 +1935,24 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   const int en = st + (ipe - ipb);
   const int q_len = a.max_q_len > 1 ? min(max(qo_e - qo, 0), a.max_q_len) : 1;
   // A split that does not hold this sequence (none recorded yet: chunk 0, or
-  // another kv_indptr) is skipped: every slot read below is then < 2 * n_wg
-  // <= 2 * units, inside the partial buffers.
+  // another kv_indptr) is skipped: every slot read below is then below
+  // batch * spec + 2 * n_wg <= batch * spec + 2 * units, inside the partial
+  // buffers.
   if (en <= st || tau >= q_len) return;
   if (geo.chunk < 1 || geo.n_wg > a.units || st < 0 || en > geo.total || (en - 1) / geo.chunk >= geo.n_wg) return;
   const int S = piece_count(st, en, geo.chunk);
   if (S <= 1) return;
-  const int chunk = geo.chunk;
-  const int qmax = a.max_q_len;
-  merge_head_wave(
-      a.part_o, a.part_lse, S, [=](int i) { return piece_slot(st, chunk, i) * qmax + tau; }, 1.0f, h,
-      a.out + ((size_t)(qo + tau) * kHeads + h) * kVDim,
-      a.lse_out != nullptr ? a.lse_out + (size_t)(qo + tau) * kHeads + h : nullptr);
+  uint16_t* const out_head = a.out + ((size_t)(qo + tau) * kHeads + h) * kVDim;
+  float* const lse_dst = a.lse_out != nullptr ? a.lse_out + (size_t)(qo + tau) * kHeads + h : nullptr;
+  if (S <= spec) {  // every piece is in
+    merge_head_wave<true>(a.part_o, a.part_lse, S, [](int) { return 0; }, 1.0f, h, out_head, lse_dst, &pre);
+  } else {
+    const int chunk = geo.chunk;
+    const int batch = a.batch;
+    merge_head_wave(
+        a.part_o, a.part_lse, S, [=](int i) { return part_slot(b, i, st, chunk, spec, batch) * qmax + tau; }, 1.0f,
+        h, out_head, lse_dst);
+  }
 }
 
 // Merge of caller-provided partials (natural-log lse), one wave per (sequence, head).

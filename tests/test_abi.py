@@ -58,13 +58,20 @@ def _params(**kw):
 def test_workspace_size_is_host_arithmetic():
     p = _params(batch=64, num_units=256)
     n = B.mla_decode_workspace_size(p)
-    # counters (64 int32 + 8 int32 of split record, padded to 256 B) + partial O (2*256*16*512 fp32)
-    # + partial lse (2*256*16 fp32)
-    assert n == 512 + 2 * 256 * 16 * 512 * 4 + 2 * 256 * 16 * 4
+    # counters (64 int32 + 8 int32 of split record, padded to 256 B), then the partial slots: two per
+    # share (2*256) and, with 256 shares for 64 sequences, 256/64 = 4 per sequence (64*4); partial O
+    # 16*512 fp32 and partial lse 16 fp32 per slot
+    slots = 2 * 256 + 64 * 4
+    assert n == 512 + slots * 16 * 512 * 4 + slots * 16 * 4
+    # fewer than two shares per sequence: no per-sequence slots
     assert B.mla_decode_workspace_size(_params(batch=1000, num_units=4)) == 4096 + 2 * 4 * 16 * 512 * 4 + 512
+    # 8 per sequence at most: with 64 shares per sequence, none
+    assert B.mla_decode_workspace_size(_params(batch=32, num_units=256)) == \
+        256 + (512 + 32 * 8) * 16 * 512 * 4 + (512 + 32 * 8) * 16 * 4
+    assert B.mla_decode_workspace_size(_params(batch=4, num_units=256)) == 256 + 512 * 16 * 512 * 4 + 512 * 16 * 4
     # with several query tokens every partial slot has a row per token
     assert B.mla_decode_workspace_size(_params(batch=64, total_q=128, num_units=256, max_q_len=2)) == \
-        512 + 2 * 2 * 256 * 16 * 512 * 4 + 2 * 2 * 256 * 16 * 4
+        512 + 2 * slots * 16 * 512 * 4 + 2 * slots * 16 * 4
 
 
 @pytest.mark.parametrize(
