@@ -484,10 +484,11 @@ __device__ __forceinline__ Geo make_geo(const Geo& g0, int batch, int units, int
   return g;
 }
 
-// Partial slot of the i-th piece of a sequence occupying [st, en) of the
-// split space (en > st).  Workgroup k writes the piece of its first sequence to slot 2k
-// and the piece of its last sequence to slot 2k+1; a sequence that starts
-// exactly at a share boundary is the first sequence of that share.
+// Share slot of the i-th piece of a sequence occupying [st, en) of the split
+// space (en > st): workgroup k has two, 2k for the piece of its first
+// sequence and 2k+1 for the piece of its last one; a sequence that starts
+// exactly at a share boundary is the first sequence of that share.  (The
+// partial buffers put the per-sequence slots of part_slot before these.)
 __device__ __forceinline__ int piece_slot(int st, int chunk, int i) {
   const int k1 = st / chunk;
   return i == 0 ? 2 * k1 + (st != k1 * chunk ? 1 : 0) : 2 * (k1 + i);
