@@ -586,15 +586,16 @@ def test_split_rule(gpu, lens, page, units, cost):
     assert_parity(ref[seqs], to64(out)[seqs], f"split rule {lens[:2]} p{page} u{units}")
 
 
-@pytest.mark.parametrize("units,q_len", [(16, 1), (32, 1), (64, 1), (32, 2)])
+@pytest.mark.parametrize("units,q_len,qd,kd", [(16, 1, "bf16", "fp8"), (32, 1, "bf16", "fp8"), (64, 1, "bf16", "fp8"),
+                                             (32, 2, "bf16", "fp8"), (32, 2, "bf16", "bf16"), (64, 2, "fp8", "fp8")])
 @pytest.mark.parametrize("flags", [0, binding.MLA_FLAG_FUSED_MERGE], ids=["merge_launch", "fused_merge"])
-def test_per_sequence_partial_slots(gpu, units, q_len, flags):
+def test_per_sequence_partial_slots(gpu, units, q_len, qd, kd, flags):
     """The first units // batch pieces of each sequence (2 to 8 of them) sit in slots of their own, which the
     merge launch loads before it reads the split; further pieces stay in their shares' slots.  Lengths are
     mixed so that sequences have one piece (nothing to merge), fewer, as many and more pieces than those
     slots, with the per-sequence cost in the split (lengths differ)."""
     lens = [700, 64, 2500, 1, 1300, 4000, 333, 1800]
-    spec = synth.CaseSpec(batch=len(lens), q_dtype="bf16", kv_dtype="fp8", lengths=lens, permuted=True,
+    spec = synth.CaseSpec(batch=len(lens), q_dtype=qd, kv_dtype=kd, lengths=lens, permuted=True,
                           q_lens=[q_len] * len(lens) if q_len > 1 else None, extra_pool_rows=11, seed=8800 + units)
     case = synth.make_case(spec)
     dc = DevCase(case, gpu)
@@ -602,9 +603,9 @@ def test_per_sequence_partial_slots(gpu, units, q_len, flags):
     ref = oracle_ref(case, causal=causal)
     for rep in range(2):  # the second run finds the first run's partials in the slots
         log(f"[per-sequence slots units={units} q_len={q_len} flags={flags} run {rep}]")
-        out = dc.run(num_units=units, min_chunk=32, flags=flags, causal=causal)
+        out = dc.run(num_units=units, min_chunk=32, flags=flags, causal=causal, q_cast=qd == "fp8")
         torch.cuda.synchronize()
-        assert_parity(ref, to64(out), f"slots u{units} q{q_len} f{flags} r{rep}")
+        assert_parity(ref, to64(out), f"slots {qd}/{kd} u{units} q{q_len} f{flags} r{rep}")
 
 
 def test_merge_before_any_attention_writes_nothing(gpu):
