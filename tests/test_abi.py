@@ -4,6 +4,8 @@ header declares, and rejects bad arguments on the host before any HIP call."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 import torch
@@ -242,3 +244,21 @@ def test_binding_has_no_cpu_fallback():
 def test_widened_params_pass_host_validation(kw):
     # accepted shapes get a workspace size with explicit units (no device query needed)
     assert B.mla_decode_workspace_size(_params(**kw)) > 0
+
+
+def test_abi_from_plain_c(tmp_path):
+    """The header and library serve a plain C99 program (gcc, no HIP compiler, no Python): version, status
+    strings, workspace sizing and host-side rejections, all without a device."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(B.library_path())
+    exe = str(tmp_path / "abi_from_c")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+           "-I", "/opt/rocm/include", os.path.join(root, "tests", "c", "abi_from_c.c"), "-L", libdir, "-lmla_decode",
+           f"-Wl,-rpath,{libdir}", "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    res = subprocess.run([exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.count("ok  ") == 10, res.stdout
