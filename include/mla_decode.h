@@ -152,8 +152,9 @@ typedef struct {
   uint64_t off_counters; /* int32 [batch]: arrivals per split sequence (fused merge), left at 0 after each
                             run; then 8 int32: the split of the last attention launch, for the merge */
   uint64_t off_part_o;   /* float32 [(2 * num_units + batch * S) * max_q_len, 16, 512]: normalised split
-                            partials; S = num_units / batch if that is 2 to 8, else 0: slots per
-                            sequence that the merge loads before it reads the split */
+                            partials; S = min(16, num_units / batch) if num_units >= 2 * batch,
+                            else 0: slots per sequence that the merge loads before it reads the
+                            split */
   uint64_t off_part_lse; /* float32 [(2 * num_units + batch * S) * max_q_len, 16]: log2-sum-exp of each */
 } mla_decode_plan_t;
 

@@ -77,13 +77,12 @@ struct Layout {
 int32_t max_q_of(const mla_decode_params* p) { return p->max_q_len > 0 ? p->max_q_len : 1; }
 
 // Partial slots of their own per sequence (mla::part_slot): as many as a
-// sequence has pieces when every sequence has the same length, where that is
-// 2 to mla::kMaxSpec; else none (a sequence with more pieces than the merge
-// loads ahead gains nothing from the slots).
+// sequence has pieces when every sequence has the same length, at most
+// mla::kMaxSpec, where that is at least 2; else none.
 int32_t spec_of(const mla_decode_params* p, int32_t units) {
   if ((int64_t)units < 2 * (int64_t)p->batch) return 0;
   const int32_t s = units / p->batch;
-  return s <= mla::kMaxSpec ? s : 0;
+  return s <= mla::kMaxSpec ? s : mla::kMaxSpec;
 }
 
 // Partials: spec slots per sequence, then two per workgroup share, each with

@@ -502,9 +502,10 @@ __device__ __forceinline__ int piece_count(int st, int en, int chunk) {
 // sequence have slots of their own, b * spec + i, which the merge launch can
 // load before it has read the split (its first round trip); the others
 // follow them, in the slots of their workgroup shares (piece_slot).  The
-// library chooses spec = units / batch (the pieces of a sequence when every
-// sequence has the same length) where that is 2 to kMaxSpec, else 0.
-constexpr int kMaxSpec = 8;
+// library chooses spec = min(units / batch, kMaxSpec) (the pieces of a
+// sequence when every sequence has the same length) where units >= 2 * batch,
+// else 0.
+constexpr int kMaxSpec = 16;
 __device__ __forceinline__ int part_slot(int b, int i, int st, int chunk, int spec, int batch) {
   return i < spec ? b * spec + i : batch * spec + piece_slot(st, chunk, i);
 }
@@ -531,31 +532,46 @@ struct MergePre {
 // a NaN lse (NaN inputs) gives a NaN weight and a NaN result.
 // With lse_dst, lane 0 also stores the merged natural-log sum-exp,
 // (M + log2 sum_i 2^(lse_i - M)) ln 2, or -inf when every piece is empty.
-// kPre: all S <= kMaxSpec pieces are already loaded in *pre (same
-// arithmetic; a mix of loaded and preloaded pieces would join the two paths
-// on values still in flight, and the compiler waits for them there).
+// kPre: all S <= kMaxSpec pieces are already loaded in *pre (the same
+// arithmetic in one pass; a mix of loaded and preloaded pieces would join the
+// two paths on values still in flight, and the compiler waits for them there).
 template <bool kPre = false, class SlotFn>
 __device__ void merge_head_wave(const float* __restrict__ part_o, const float* __restrict__ part_lse, int S,
                                 SlotFn slot_of, float lse_mul, int h, uint16_t* __restrict__ out_head,
                                 float* __restrict__ lse_dst, const MergePre* pre = nullptr) {
   const int lane = threadIdx.x & 63;
   constexpr int kBatch = 8;
-  static_assert(kBatch == kMaxSpec, "preloaded pieces fill the first batch");
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY;
   float wsum = 0.f;
   for (int i0 = 0; i0 < S; i0 += 64) {
     const int n = min(64, S - i0);
+    if constexpr (kPre) {  // S <= kMaxSpec: one chunk, every piece in *pre
+      const float v = (lane < n) ? pre->lse * lse_mul : -INFINITY;
+      M = wave_max(v);
+      const float wt = (v == -INFINITY) ? 0.f : fast_exp2(v - M);
+      wsum = wave_sum(wt);
+#pragma unroll
+      for (int u = 0; u < kMaxSpec / 2; ++u)
+        if (u < n) {
+          const float wj = __shfl(wt, u);
+          acc0 += wj != 0.f ? wj * pre->a[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc1 += wj != 0.f ? wj * pre->b[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      if (n > kMaxSpec / 2) {
+#pragma unroll
+        for (int u = kMaxSpec / 2; u < kMaxSpec; ++u)
+          if (u < n) {
+            const float wj = __shfl(wt, u);
+            acc0 += wj != 0.f ? wj * pre->a[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc1 += wj != 0.f ? wj * pre->b[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+      break;
+    }
     f32x4_t a[kBatch], b[kBatch];
     float v;
-    if constexpr (kPre) {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        a[u] = pre->a[u];
-        b[u] = pre->b[u];
-      }
-      v = (lane < n) ? pre->lse * lse_mul : -INFINITY;
-    } else {
+    {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
         if (u < n) {
@@ -1905,8 +1921,7 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   // the split is known.  Slots past the sequence's pieces hold stale values
   // and are never used.
   MergePre pre;
-#pragma unroll
-  for (int u = 0; u < kMaxSpec; ++u) {
+  auto pre_load = [&](int u) {
     if (u < spec) {
       const f32x4_t* src = reinterpret_cast<const f32x4_t*>(
           a.part_o + ((size_t)((b * spec + u) * qmax + tau) * kHeads + h) * kVDim + lane * 8);
@@ -1916,6 +1931,12 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
       pre.a[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       pre.b[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+  };
+#pragma unroll
+  for (int u = 0; u < kMaxSpec / 2; ++u) pre_load(u);
+  if (spec > kMaxSpec / 2) {
+#pragma unroll
+    for (int u = kMaxSpec / 2; u < kMaxSpec; ++u) pre_load(u);
   }
   pre.lse = lane < spec ? a.part_lse[((b * spec + lane) * qmax + tau) * kHeads + h] : -INFINITY;
   // Every index this wave needs is loaded in the same round trip: a load

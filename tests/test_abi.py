@@ -67,10 +67,11 @@ def test_workspace_size_is_host_arithmetic():
     assert n == 512 + slots * 16 * 512 * 4 + slots * 16 * 4
     # fewer than two shares per sequence: no per-sequence slots
     assert B.mla_decode_workspace_size(_params(batch=1000, num_units=4)) == 4096 + 2 * 4 * 16 * 512 * 4 + 512
-    # 8 per sequence at most: with 64 shares per sequence, none
+    # 8 per sequence with 8 shares per sequence; 16 at most (64 shares per sequence)
     assert B.mla_decode_workspace_size(_params(batch=32, num_units=256)) == \
         256 + (512 + 32 * 8) * 16 * 512 * 4 + (512 + 32 * 8) * 16 * 4
-    assert B.mla_decode_workspace_size(_params(batch=4, num_units=256)) == 256 + 512 * 16 * 512 * 4 + 512 * 16 * 4
+    assert B.mla_decode_workspace_size(_params(batch=4, num_units=256)) == \
+        256 + (512 + 4 * 16) * 16 * 512 * 4 + (512 + 4 * 16) * 16 * 4
     # with several query tokens every partial slot has a row per token
     assert B.mla_decode_workspace_size(_params(batch=64, total_q=128, num_units=256, max_q_len=2)) == \
         512 + 2 * slots * 16 * 512 * 4 + 2 * slots * 16 * 4
