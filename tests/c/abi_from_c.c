@@ -9,6 +9,27 @@
 
 static int failures = 0;
 
+/* The README's usage example, compiled here so that it keeps to the header;
+ * not called (it needs a device). */
+mla_status example_step(const void* q, const void* kv, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, const float* kv_scale, void* out, hipStream_t stream);
+mla_status example_step(const void* q, const void* kv, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, const float* kv_scale, void* out, hipStream_t stream) {
+  mla_decode_params p = {0};
+  p.batch = 64; p.total_q = 64;
+  p.num_heads = 16; p.num_kv_heads = 1; p.qk_dim = 576; p.v_dim = 512; p.page_size = 1;
+  p.q_dtype = MLA_DTYPE_BF16; p.kv_dtype = MLA_DTYPE_FP8_E4M3FN;
+  size_t bytes = mla_decode_workspace_size(&p);
+  void* ws;
+  if (hipMalloc(&ws, bytes) != hipSuccess) return MLA_ERR_HIP;
+  mla_decode_plan_t plan;
+  mla_status st = mla_decode_plan(&p, ws, bytes, stream, &plan);
+  if (st != MLA_OK) return st;
+  st = mla_decode_run(&plan, q, kv, qo_indptr, kv_indptr, kv_indices, NULL, kv_scale, 1.0f / 24.0f, out, stream);
+  if (st != MLA_OK) fprintf(stderr, "%s\n", mla_status_string(st));
+  return st;
+}
+
 static void check(int ok, const char* what) {
   printf("%s %s\n", ok ? "ok  " : "FAIL", what);
   if (!ok) ++failures;

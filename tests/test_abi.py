@@ -258,7 +258,7 @@ def test_abi_from_plain_c(tmp_path):
     exe = str(tmp_path / "abi_from_c")
     cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
            "-I", "/opt/rocm/include", os.path.join(root, "tests", "c", "abi_from_c.c"), "-L", libdir, "-lmla_decode",
-           f"-Wl,-rpath,{libdir}", "-o", exe]
+           f"-Wl,-rpath,{libdir}", "-L", "/opt/rocm/lib", "-lamdhip64", "-o", exe]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     res = subprocess.run([exe], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
