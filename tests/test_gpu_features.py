@@ -248,3 +248,21 @@ def test_large_pages(gpu, ps):
         out = dc.run(num_units=units, min_chunk=32)
         torch.cuda.synchronize()
         assert_parity(ref, to64(out), f"ps{ps} u{units}")
+
+
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_most_tokens_per_sequence(gpu, qd, kd):
+    """max_q_len 16, the most the library takes: eight two-token passes over each piece.  A 9-row sequence
+    with 16 causal tokens leaves its first 7 tokens without a visible row (zeros); a long one is split."""
+    lens, q_lens = [9, 3000, 600], [16, 16, 5]
+    spec = synth.CaseSpec(batch=3, q_dtype=qd, kv_dtype=kd, lengths=lens, q_lens=q_lens, permuted=True,
+                          extra_pool_rows=7, seed=3700 + PAIRS.index((qd, kd)))
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case, causal=True)
+    for units, flags in ((1, 0), (32, 0), (256, binding.MLA_FLAG_FUSED_MERGE)):
+        log(f"[16 tokens {qd}/{kd} units={units} flags={flags}]")
+        out = dc.run(num_units=units, min_chunk=32, flags=flags, causal=True, q_cast=qd == "fp8")
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"16 tokens {qd}/{kd} u{units} f{flags}")
+        assert torch.equal(out[:7].cpu().float(), torch.zeros(7, 16, 512))

@@ -678,3 +678,19 @@ def test_graph_capture_and_replay(gpu, qd, flags):
     case_b = synth.Case(spec, case.q_bf16, case.kv, case.kv_scale, case.qo_indptr, indptr_b.cpu(), case.kv_indices,
                         torch.tensor(lens_b), case.kv_last_page_len)
     assert_parity(oracle_ref(case_b), to64(out_g), f"graph lengths B {qd} flags={flags}")
+
+
+@pytest.mark.parametrize("qd,kd", [("bf16", "fp8"), ("fp8", "fp8")])
+def test_one_sequence_over_every_workgroup(gpu, qd, kd):
+    """A single sequence of 65,573 rows split over 256 shares: the merge folds 256 pieces in four chunks of 64
+    (the per-sequence slots hold only the first 16)."""
+    spec = synth.CaseSpec(batch=1, q_dtype=qd, kv_dtype=kd, lengths=[65573], permuted=True, extra_pool_rows=5,
+                          seed=3800)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units, flags in ((256, 0), (256, binding.MLA_FLAG_FUSED_MERGE), (100, 0)):
+        log(f"[one sequence {qd}/{kd} units={units} flags={flags}]")
+        out = dc.run(num_units=units, min_chunk=32, flags=flags, q_cast=qd == "fp8")
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"one sequence {qd}/{kd} u{units} f{flags}")
