@@ -37,6 +37,21 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_binding_constants_match_header():
+    """Every MLA_* constant the binding restates has the header's value (macros and enumerators)."""
+    text = open(HEADER).read()
+    values = {}
+    # macros: a number, or (N << M), with an optional u suffix
+    for name, num, shift in re.findall(r"#define\s+(MLA_[A-Z0-9_]+)\s+\(?([0-9]+)u?(?:\s*<<\s*([0-9]+))?\)?", text):
+        values[name] = int(num) << int(shift or 0)
+    for name, value in re.findall(r"\b(MLA_[A-Z0-9_]+)\s*=\s*([0-9]+)", text):  # enumerators
+        values[name] = int(value)
+    checked = [name for name in B.__all__ if name in values]
+    for name in checked:
+        assert getattr(B, name) == values[name], name
+    assert len(checked) >= 13, sorted(values)
+
+
 def test_struct_layout_matches_header():
     # 13 int32 fields and one float; the plan carries params + pointer + size + 2 int32 + 3 offsets
     assert ctypes.sizeof(B.MlaDecodeParams) == 56
