@@ -25,6 +25,8 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments (up to 16 dwords) are preloaded into SGPRs at dispatch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -333,7 +333,9 @@ mla_status mla_decode_merge(const mla_decode_plan_t* plan, const int32_t* qo_ind
   mla_status st = make_args(plan, qo_indptr, kv_indptr, out, lse_out, stream, &a);
   if (st != MLA_OK) return st;
   if (a.fused) return MLA_OK;  // the attention launch merged already
-  hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(a.batch, mla::kHeads, a.max_q_len), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(mla::mla_merge_split_kernel, dim3(a.batch, mla::kHeads, a.max_q_len), dim3(64), 0, stream,
+                     a.counters + a.batch, a.kv_indptr, a.qo_indptr, a.part_o, a.part_lse, a.spec, a.max_q_len,
+                     a.units, a.batch, a);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -1909,13 +1909,20 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(Args a) {
 
 // Separate merge launch: one wave per (sequence, head, token); sequences that
 // were not split were finished by the attention kernel and are skipped.
-__global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
+// The arguments the first round trip needs come first, as scalars: the
+// library is built to have the command processor preload leading kernel
+// arguments into scalar registers, so those loads go out without waiting for
+// the kernel-argument segment (the Args copy serves the rest).
+__global__ __launch_bounds__(64) void mla_merge_split_kernel(const int32_t* __restrict__ rec,
+                                                             const int32_t* __restrict__ kv_indptr,
+                                                             const int32_t* __restrict__ qo_indptr,
+                                                             const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_lse, int32_t spec,
+                                                             int32_t qmax, int32_t units, int32_t batch, Args a) {
   const int b = blockIdx.x;
   const int h = blockIdx.y;
   const int tau = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int spec = a.spec;
-  const int qmax = a.max_q_len;
   // The sequence's first `spec` pieces have slots that depend on b alone
   // (part_slot): their loads go out with the first round trip below, before
   // the split is known.  Slots past the sequence's pieces hold stale values
@@ -1924,7 +1931,7 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
   auto pre_load = [&](int u) {
     if (u < spec) {
       const f32x4_t* src = reinterpret_cast<const f32x4_t*>(
-          a.part_o + ((size_t)((b * spec + u) * qmax + tau) * kHeads + h) * kVDim + lane * 8);
+          part_o + ((size_t)((b * spec + u) * qmax + tau) * kHeads + h) * kVDim + lane * 8);
       pre.a[u] = src[0];
       pre.b[u] = src[1];
     } else {
@@ -1938,41 +1945,40 @@ __global__ __launch_bounds__(64) void mla_merge_split_kernel(Args a) {
 #pragma unroll
     for (int u = kMaxSpec / 2; u < kMaxSpec; ++u) pre_load(u);
   }
-  pre.lse = lane < spec ? a.part_lse[((b * spec + lane) * qmax + tau) * kHeads + h] : -INFINITY;
+  pre.lse = lane < spec ? part_lse[((b * spec + lane) * qmax + tau) * kHeads + h] : -INFINITY;
   // Every index this wave needs is loaded in the same round trip: a load
   // written after one of the early exits below is issued only once the values
   // that decide the exit have arrived.
-  const int32_t* gr = a.counters + a.batch;  // the split the attention launch used
+  const int32_t* gr = rec;  // the split the attention launch used (after the arrival counters)
   Geo geo;
   geo.base = gr[0];
   geo.cost = gr[1];
   geo.total = gr[2];
   geo.chunk = gr[3];
   geo.n_wg = gr[4];
-  const int ipb = a.kv_indptr[b];
-  const int ipe = a.kv_indptr[b + 1];
-  const int qo = a.qo_indptr[b];
-  const int qo_e = a.qo_indptr[b + 1];
+  const int ipb = kv_indptr[b];
+  const int ipe = kv_indptr[b + 1];
+  const int qo = qo_indptr[b];
+  const int qo_e = qo_indptr[b + 1];
   const int st = ipb - geo.base + geo.cost * b;
   const int en = st + (ipe - ipb);
-  const int q_len = a.max_q_len > 1 ? min(max(qo_e - qo, 0), a.max_q_len) : 1;
+  const int q_len = qmax > 1 ? min(max(qo_e - qo, 0), qmax) : 1;
   // A split that does not hold this sequence (none recorded yet: chunk 0, or
   // another kv_indptr) is skipped: every slot read below is then below
   // batch * spec + 2 * n_wg <= batch * spec + 2 * units, inside the partial
   // buffers.
   if (en <= st || tau >= q_len) return;
-  if (geo.chunk < 1 || geo.n_wg > a.units || st < 0 || en > geo.total || (en - 1) / geo.chunk >= geo.n_wg) return;
+  if (geo.chunk < 1 || geo.n_wg > units || st < 0 || en > geo.total || (en - 1) / geo.chunk >= geo.n_wg) return;
   const int S = piece_count(st, en, geo.chunk);
   if (S <= 1) return;
   uint16_t* const out_head = a.out + ((size_t)(qo + tau) * kHeads + h) * kVDim;
   float* const lse_dst = a.lse_out != nullptr ? a.lse_out + (size_t)(qo + tau) * kHeads + h : nullptr;
   if (S <= spec) {  // every piece is in
-    merge_head_wave<true>(a.part_o, a.part_lse, S, [](int) { return 0; }, 1.0f, h, out_head, lse_dst, &pre);
+    merge_head_wave<true>(part_o, part_lse, S, [](int) { return 0; }, 1.0f, h, out_head, lse_dst, &pre);
   } else {
     const int chunk = geo.chunk;
-    const int batch = a.batch;
     merge_head_wave(
-        a.part_o, a.part_lse, S, [=](int i) { return part_slot(b, i, st, chunk, spec, batch) * qmax + tau; }, 1.0f,
+        part_o, part_lse, S, [=](int i) { return part_slot(b, i, st, chunk, spec, batch) * qmax + tau; }, 1.0f,
         h, out_head, lse_dst);
   }
 }
