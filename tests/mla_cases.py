@@ -58,7 +58,8 @@ class DevCase:
         return binding.Decoder(self.batch, self.q_dtype, self.kv_dtype, self.dev, **kw)
 
     def run(self, dec: binding.Decoder | None = None, out: torch.Tensor | None = None, q_cast: bool = False,
-            causal: bool = False, paged: bool | None = None, **kw) -> torch.Tensor:
+            causal: bool = False, paged: bool | None = None, sm_scale: float = oracle.SM_SCALE,
+            **kw) -> torch.Tensor:
         """One decode step; with q_cast the fp8 Q is cast inside the attention kernel from the bf16 Q.
 
         Pages of more than one row go through mla_decode_run_paged with the case's last-page lengths
@@ -73,7 +74,7 @@ class DevCase:
         q = self.q_bf16 if q_cast else self.q
         use_paged = self.page_size > 1 if paged is None else paged
         dec.run(q, self.kv, self.qo_indptr, self.kv_indptr, self.kv_indices, self.q_scale, self.kv_scale,
-                oracle.SM_SCALE, out, kv_last_page_len=self.kv_last_page_len if use_paged else None)
+                sm_scale, out, kv_last_page_len=self.kv_last_page_len if use_paged else None)
         return out
 
 

@@ -15,7 +15,7 @@ import torch
 import oracle
 from mla_decode_paged_split_amd import binding, synth
 
-from mla_cases import DevCase, Timer, assert_parity, log, oracle_ref, to64
+from mla_cases import DevCase, Timer, assert_parity, compare, log, oracle_ref, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -241,6 +241,56 @@ def test_dominant_last_row(gpu, qd, kd):
             v = vals[int(case.kv_indices[int(case.kv_indptr[b + 1]) - 1]), :512]
             assert np.abs(got[b] - v[None, :]).max() <= 2.0 ** -8 * np.abs(v).max(), (qd, kd, units, b)
         log(f"  dominant last row {qd}/{kd} units={units}: ok")
+
+
+@pytest.mark.parametrize("sm_scale", [0.25 / 24, 3.0 / 24])
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_scale_arguments(gpu, qd, kd, sm_scale):
+    """sm_scale, q_scale and kv_scale away from their usual values: the scores are
+    sm_scale * q_scale * kv_scale * (q . k) and the output is kv_scale times the softmax-weighted rows, so a
+    scale applied in the wrong place, twice or not at all moves the result far outside the tolerance."""
+    spec = synth.CaseSpec(batch=4, q_dtype=qd, kv_dtype=kd, lengths=[700, 1, 2100, 64], permuted=True, seed=2700)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    q_bits = case.q_bits().numpy()
+    q_scale = kv_scale = None
+    if qd == "fp8":
+        q_bits = oracle.bf16_bits_to_fp8_bits(q_bits)
+        q_scale = 0.5
+        dc.q_scale = torch.tensor([q_scale], dtype=torch.float32, device=gpu)
+    if kd == "fp8":
+        kv_scale = float(case.kv_scale[0]) * 2.0
+        dc.kv_scale = torch.tensor([kv_scale], dtype=torch.float32, device=gpu)
+    ref = oracle.mla_decode(q_bits, case.kv_bits().numpy(), case.qo_indptr.numpy(), case.kv_indptr.numpy(),
+                            case.kv_indices.numpy(), q_dtype=qd, kv_dtype=kd, q_scale=q_scale, kv_scale=kv_scale,
+                            sm_scale=sm_scale)
+    default = oracle.mla_decode(q_bits, case.kv_bits().numpy(), case.qo_indptr.numpy(), case.kv_indptr.numpy(),
+                                case.kv_indices.numpy(), q_dtype=qd, kv_dtype=kd,
+                                q_scale=1.0 if qd == "fp8" else None,
+                                kv_scale=float(case.kv_scale[0]) if kd == "fp8" else None)
+    assert not compare(default, ref, "scaled against default scales")["elem_ok"]  # the scales matter here
+    for units in (1, 64):
+        out = dc.run(num_units=units, min_chunk=32, sm_scale=sm_scale)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"scales {qd}/{kd} sm={sm_scale:.4f} u{units}")
+
+
+@pytest.mark.parametrize("qd,kd", PAIRS)
+def test_wide_range_q(gpu, qd, kd):
+    """Q values spread over 2^-12 .. 2^6 in magnitude in every head: the scores span thousands, so the running
+    maximum jumps often and by far more than the speculative weights' slack (each such step is redone with
+    the new maximum)."""
+    spec = synth.CaseSpec(batch=3, q_dtype=qd, kv_dtype=kd, lengths=[1500, 300, 4100], permuted=True, seed=2800)
+    case = synth.make_case(spec)
+    g = torch.Generator().manual_seed(2801)
+    mag = torch.pow(2.0, torch.empty(case.q_bf16.shape).uniform_(-12.0, 6.0, generator=g))
+    case.q_bf16 = (case.q_bf16.float() * mag).to(torch.bfloat16)
+    dc = DevCase(case, gpu)
+    ref = oracle_ref(case)
+    for units in (1, 32, 256):
+        out = dc.run(num_units=units, min_chunk=32)
+        torch.cuda.synchronize()
+        assert_parity(ref, to64(out), f"wide-range q {qd}/{kd} u{units}")
 
 
 @pytest.mark.parametrize("qd,kd", PAIRS)
