@@ -293,6 +293,30 @@ def test_wide_range_q(gpu, qd, kd):
         assert_parity(ref, to64(out), f"wide-range q {qd}/{kd} u{units}")
 
 
+@pytest.mark.parametrize("qd,kd", [("bf16", "bf16"), ("fp8", "fp8")])
+def test_pool_beyond_2gib(gpu, qd, kd):
+    """The same rows at the end of a KV pool larger than 2 GiB (indices rebased) give the same bits as in a
+    compact pool: row addresses are formed in 64 bits."""
+    spec = synth.CaseSpec(batch=3, q_dtype=qd, kv_dtype=kd, lengths=[300, 1, 2000], permuted=True, seed=2900)
+    case = synth.make_case(spec)
+    dc = DevCase(case, gpu)
+    small = dc.run(num_units=64, min_chunk=32).clone()
+    rows = dc.kv.shape[0]
+    row_bytes = dc.kv.shape[1] * dc.kv.element_size()
+    total = (2 ** 31) // row_bytes + 2 * rows + 1024  # the case's rows start past byte 2^31
+    base = total - rows
+    assert base * row_bytes > 2 ** 31
+    big = torch.empty((total, dc.kv.shape[1]), dtype=dc.kv.dtype, device=gpu)
+    big[base:].copy_(dc.kv)
+    dc.kv = big
+    dc.kv_indices = dc.kv_indices + base
+    moved = dc.run(num_units=64, min_chunk=32)
+    torch.cuda.synchronize()
+    assert torch.equal(small.view(torch.int16), moved.view(torch.int16))
+    assert_parity(oracle_ref(case), to64(moved), f"pool beyond 2 GiB {qd}/{kd}")
+    del big
+
+
 @pytest.mark.parametrize("qd,kd", PAIRS)
 def test_shared_and_repeated_pages(gpu, qd, kd):
     """Sequences that share pages (a common prefix, as with prefix caching) and a sequence that lists
